@@ -1,0 +1,27 @@
+"""Plain fp64 CPU oracle for tree-verify MLA-absorb attention and post-accept KV compaction.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the tests, the smoke check and the benchmark's CPU
+baseline may import this package.  It shares no code with the HIP library and imports nothing
+from it; the two meet only in the seeded arrays of the ``synth`` module.
+
+Everything is written out from its definition, in float64, with no blocking or fusion:
+
+* ``verify_attn``   -- masked softmax attention in the absorbed MLA form.
+* ``compact_kv``    -- the out-of-place gather of the kept tree rows into the prefix.
+
+Every function is pinned by the CPU tests (brute force over all small trees, causal attention
+for a chain, per-path causal attention, closed forms, lse merge, equivariances, the absorb
+identity, and the race example).
+"""
+from .verify import (  # noqa: F401
+    DEFAULT_SCALE,
+    ancestor_or_self,
+    bf16_bits_to_f64,
+    masked_softmax_attention,
+    scores_absorbed,
+    verify_attn,
+    verify_attn_f64,
+    verify_attn_stream,
+    visibility,
+)
+from .compact import compact_kv, validate_keep  # noqa: F401

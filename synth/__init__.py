@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs for tree-verify MLA-absorb attention and KV compaction.
+
+This module holds none of the method's arithmetic.  It only draws inputs: bf16 activations
+(standard normal, rounded to bf16 by round-to-nearest-even on the fp32 bits), draft trees as
+``parents[]`` arrays, and an accepted root-to-leaf path per stream.  Both the fp64 oracle and the
+HIP path consume exactly these arrays, bit for bit.
+
+Shapes follow the pages' engine ("Race Conditions, Buffer Aliasing, and the Architecture of a
+Native DDTree Inference Engine", section "The Cache Compaction Problem"): one latent cache per
+stream, the committed prefix in rows ``[0, P)`` and tree node ``i`` in row ``P + i``; a child
+always has a larger node index than its parent.  The tree sizes respect the limits of the
+tree builder on "Building the Foundation: Architecting a Native CUDA DDTree Inference Engine",
+section "The Single-Threaded Heap Design" (budget at most 64, depth at most 15).
+
+Every random draw uses ``numpy.random.Generator(PCG64(SeedSequence([seed, stream, tag])))`` so that
+any stream can be regenerated on its own.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+HEADS = 64
+D_LATENT = 512
+D_ROPE = 64
+MAX_DEPTH = 15
+
+TAG_Q_LAT, TAG_Q_PE, TAG_CKV, TAG_KPE, TAG_PARENTS, TAG_LEAF = 0, 1, 2, 3, 4, 5
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: ``streams`` independent requests sharing one launch."""
+
+    name: str
+    streams: int
+    prefix: int
+    q_len: int
+    tree: str = "uniform"  # "uniform" or "chain70"
+    seed: int = 0
+    heads: int = HEADS
+
+    @property
+    def kv_rows(self) -> int:
+        return self.prefix + self.q_len
+
+
+# The five seeded workloads: small single stream; eight mid-length streams; many small query
+# blocks; one long chain-heavy stream; sixty-four long streams followed by compaction.
+WORKLOADS: dict[str, Workload] = {
+    w.name: w
+    for w in (
+        Workload("s1-p256-q9", 1, 256, 9, "uniform", seed=1),
+        Workload("s8-p1024-q33", 8, 1024, 33, "uniform", seed=2),
+        Workload("s64-p1024-q9", 64, 1024, 9, "uniform", seed=3),
+        Workload("s1-p4096-q33-chain", 1, 4096, 33, "chain70", seed=4),
+        Workload("s64-p4096-q33", 64, 4096, 33, "uniform", seed=5),
+    )
+}
+HEADLINE = "s64-p4096-q33"
+
+
+def rng_for(seed: int, stream: int, tag: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, tag])))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round-to-nearest-even), returned as uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_normal(rng: np.random.Generator, shape) -> np.ndarray:
+    return f32_to_bf16_bits(rng.standard_normal(size=shape, dtype=np.float32))
+
+
+def sample_parents(rng: np.random.Generator, q_len: int, tree: str = "uniform",
+                   max_depth: int = MAX_DEPTH) -> np.ndarray:
+    """Draw a draft tree as ``parents[]``: node 0 is the root, every parent index is smaller.
+
+    ``uniform``: parent of node i drawn uniformly from [0, i-1]; if that parent already sits at
+    the depth cap, redraw uniformly among the earlier nodes below the cap.
+    ``chain70``: with probability 0.7 the parent is node i-1 (when it is below the cap), else the
+    uniform rule.
+    """
+    parents = np.full(q_len, -1, dtype=np.int32)
+    depth = np.zeros(q_len, dtype=np.int32)
+    for i in range(1, q_len):
+        if tree == "chain70" and rng.random() < 0.7 and depth[i - 1] < max_depth:
+            p = i - 1
+        else:
+            p = int(rng.integers(0, i))
+            if depth[p] >= max_depth:
+                ok = np.nonzero(depth[:i] < max_depth)[0]
+                p = int(ok[rng.integers(0, len(ok))])
+        parents[i] = p
+        depth[i] = depth[p] + 1
+    return parents
+
+
+def accepted_path(rng: np.random.Generator, parents: np.ndarray) -> np.ndarray:
+    """A root-to-leaf path (node indices, strictly increasing), leaf drawn uniformly."""
+    q = len(parents)
+    has_child = np.zeros(q, dtype=bool)
+    has_child[parents[1:]] = True
+    leaves = np.nonzero(~has_child)[0]
+    node = int(leaves[rng.integers(0, len(leaves))])
+    path = []
+    while node >= 0:
+        path.append(node)
+        node = int(parents[node])
+    return np.array(path[::-1], dtype=np.int32)
+
+
+@dataclass
+class Batch:
+    """Inputs for one launch, bf16 payloads stored as uint16 bit patterns."""
+
+    workload: Workload
+    q_lat: np.ndarray   # uint16 [S, Q, H, 512]
+    q_pe: np.ndarray    # uint16 [S, Q, H, 64]
+    ckv: np.ndarray     # uint16 [S, L, 512]
+    kpe: np.ndarray     # uint16 [S, L, 64]
+    parents: np.ndarray  # int32 [S, Q]
+    keep: np.ndarray    # int32 [S, Q]  (accepted path, padded with -1)
+    n_keep: np.ndarray  # int32 [S]
+    extra: dict = field(default_factory=dict)
+
+
+def make_batch(w: Workload, streams: int | None = None, with_path: bool = True) -> Batch:
+    """Generate the inputs of workload ``w`` (optionally only its first ``streams`` streams)."""
+    s_count = w.streams if streams is None else streams
+    q, l, h = w.q_len, w.kv_rows, w.heads
+    q_lat = np.empty((s_count, q, h, D_LATENT), np.uint16)
+    q_pe = np.empty((s_count, q, h, D_ROPE), np.uint16)
+    ckv = np.empty((s_count, l, D_LATENT), np.uint16)
+    kpe = np.empty((s_count, l, D_ROPE), np.uint16)
+    parents = np.empty((s_count, q), np.int32)
+    keep = np.full((s_count, q), -1, np.int32)
+    n_keep = np.zeros(s_count, np.int32)
+    for s in range(s_count):
+        q_lat[s] = bf16_normal(rng_for(w.seed, s, TAG_Q_LAT), (q, h, D_LATENT))
+        q_pe[s] = bf16_normal(rng_for(w.seed, s, TAG_Q_PE), (q, h, D_ROPE))
+        ckv[s] = bf16_normal(rng_for(w.seed, s, TAG_CKV), (l, D_LATENT))
+        kpe[s] = bf16_normal(rng_for(w.seed, s, TAG_KPE), (l, D_ROPE))
+        parents[s] = sample_parents(rng_for(w.seed, s, TAG_PARENTS), q, w.tree)
+        if with_path:
+            path = accepted_path(rng_for(w.seed, s, TAG_LEAF), parents[s])
+            keep[s, : len(path)] = path
+            n_keep[s] = len(path)
+    return Batch(w, q_lat, q_pe, ckv, kpe, parents, keep, n_keep)
+
+
+def random_inputs(seed: int, streams: int, prefix: int, q_len: int, heads: int = HEADS,
+                  tree: str = "uniform") -> Batch:
+    """Ad-hoc sizes for tests (same recipe as the named workloads)."""
+    return make_batch(Workload(f"adhoc-{seed}", streams, prefix, q_len, tree, seed, heads))
+
