@@ -1,0 +1,196 @@
+"""Benchmark: tree-verify MLA-absorb attention + KV compaction on one MI355X.
+
+One step = one pass of the whole hot path over one batch: ``ddtree_verify_attn_ex`` (64 heads,
+latent 512 + rope 64, tree mask from parents[]) followed by ``ddtree_compact_kv`` of each
+stream's accepted root-to-leaf path.  Inputs are seeded synthetic bf16 ~ N(0,1) (no dataset is
+involved) and are resident in HBM before the timed region starts.
+
+Prints one JSON line.  ``value`` is TFLOP/s of the verify attention counted over visible
+(query, key) pairs only, divided by the whole step time (verify + compaction).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify-attn us/call & TFLOP/s (64 heads, q_len 33, prefix 4096); % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "tree_verify_mla_absorb_amd", "csrc", "verify_attn.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "verify_attn_s64_p4096_q33_pmc.txt")
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def visible_pairs(parents: np.ndarray, prefix: int) -> int:
+    """Sum over streams and nodes of the number of visible keys: prefix + depth + 1."""
+    total = 0
+    for row in parents:
+        depth = np.zeros(len(row), np.int64)
+        for i in range(1, len(row)):
+            depth[i] = depth[row[i]] + 1
+        total += int((prefix + depth + 1).sum())
+    return total
+
+
+def algorithmic_bytes(w, streams: int) -> int:
+    """KV read once per stream + Q + out + lse + parents."""
+    s, q, l, h = streams, w.q_len, w.kv_rows, w.heads
+    return (s * l * (512 + 64) * 2 + s * q * h * (512 + 64) * 2 + s * q * h * 512 * 4 + s * q * h * 4
+            + s * q * 4)
+
+
+def read_traffic():
+    """HBM bytes per verify launch from the committed rocprofv3 counter summary, when that
+    summary was taken on the current kernel source (else None)."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_bytes or m_sha.group(1) != kernel_sha():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, flops_per_stream: float, budget_s: float = 12.0):
+    """The fp64 oracle, as it stands, on the first streams of the same workload until about
+    ``budget_s`` seconds of CPU work; scaled to TFLOP/s of algorithmic work."""
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t_total, done, flops = 0.0, 0, 0.0
+    while t_total < budget_s and done < w.streams:
+        b = synth.make_batch(w, streams=done + 1)
+        t0 = time.perf_counter()
+        oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, w.prefix, b.parents, streams=[done])
+        t_total += time.perf_counter() - t0
+        flops += 2.0 * w.heads * (576 + 512) * visible_pairs(b.parents[done:done + 1], w.prefix)
+        done += 1
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle on streams 0..{done - 1} of {w.streams} of workload {w.name} "
+                      f"({t_total:.1f} s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(streams shard across GPUs with no communication; see DESIGN.md)"}))
+        return 2
+
+    import torch
+
+    import synth
+    from tree_verify_mla_absorb_amd import _lib
+
+    name = args.workload or synth.HEADLINE
+    w = synth.WORKLOADS[name]
+    b = synth.make_batch(w)
+    dev = "cuda:0"
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q_lat, q_pe, ckv, kpe = up(b.q_lat), up(b.q_pe), up(b.ckv), up(b.kpe)
+    parents = torch.from_numpy(b.parents).to(dev)
+    keep = torch.from_numpy(b.keep).to(dev)
+    n_keep = torch.from_numpy(b.n_keep).to(dev)
+    out = torch.empty((w.streams, w.q_len, w.heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.streams, w.q_len, w.heads), dtype=torch.float32, device=dev)
+    splits = _lib.num_splits(w.prefix, w.q_len, w.streams, args.num_splits)
+    ws_bytes = _lib.workspace_size(w.prefix, w.q_len, w.streams, args.num_splits)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev_a=None, ev_b=None):
+        if ev_a is not None:
+            ev_a.record(stream)
+        _lib.verify_attn_ex(q_lat, q_pe, ckv, kpe, w.prefix, parents, out=out, lse=lse,
+                            num_splits=args.num_splits, workspace=ws, stream=stream)
+        if ev_b is not None:
+            ev_b.record(stream)
+        _lib.compact_kv(ckv, kpe, w.prefix, keep, n_keep, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(*evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    verify_ms = float(np.mean([a.elapsed_time(bb) for a, bb in evs]))
+
+    flops = 2.0 * w.heads * (576 + 512) * visible_pairs(b.parents, w.prefix)
+    tflops_step = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (verify_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+    res = {
+        "metric": METRIC,
+        "value": round(tflops_step, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "streams": w.streams, "heads": w.heads, "prefix": w.prefix,
+                   "q_len": w.q_len, "tree": w.tree, "seed": w.seed, "num_splits": splits,
+                   "step": "verify_attn + compact_kv"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "detail": {"verify_us_per_call": round(verify_ms * 1e3, 2),
+                   "compact_us_per_call_incl_gap": round((ms_step - verify_ms) * 1e3, 2),
+                   "verify_tflops": round(achieved, 2),
+                   "pct_mfma_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
+                   "algorithmic_bytes": algorithmic_bytes(w, w.streams),
+                   "hbm_gbs_algorithmic": round(algorithmic_bytes(w, w.streams) / (verify_ms * 1e-3) / 1e9, 1),
+                   "flop_visible_pairs": flops, "wall_s_timed": round(wall, 3),
+                   "kernel_source_sha256": kernel_sha()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, flops / w.streams)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,161 @@
+/*
+ * ddtree.h -- C ABI of the MI355X (gfx950) tree-verify MLA-absorb attention library.
+ *
+ * Two operations of a DDTree speculative-decoding step, both described on
+ * "Race Conditions, Buffer Aliasing, and the Architecture of a Native DDTree Inference Engine":
+ *
+ *   ddtree_verify_attn   the tree-verify attention in MLA-absorb form with visibility masking
+ *                        (section "The Mission: A Native DDTree Engine");
+ *   ddtree_compact_kv    the post-accept gather of the kept tree rows into the prefix, free of
+ *                        the in-place aliasing race (section "The Cache Compaction Problem").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor arguments are DEVICE pointers owned by the caller.  The library allocates
+ *   nothing and keeps no pointer after the call returns; buffers must stay alive until the
+ *   given HIP stream has executed the work.
+ * - bf16 tensors are passed as raw 16-bit storage (`const void*`), row-major, densely packed.
+ * - Calls are asynchronous on `stream` (NULL = the default stream) and never synchronise.
+ *   Host-side validation reads no device memory.  There is no global mutable state: calls are
+ *   re-entrant across host threads and streams.
+ * - Every call returns DDTREE_OK (0) or a negative DDTREE_ERR_* code.  Nothing throws, aborts
+ *   or exits across the ABI.  On error nothing is launched.
+ * - Data errors that only the device can see (a malformed `parents` or `keep`) never cause an
+ *   out-of-bounds access; they set a bit in the optional `dev_status` word (device int32,
+ *   bits OR-ed in; the caller clears it).
+ */
+#ifndef DDTREE_H
+#define DDTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DDTREE_VERSION 1
+
+/* Model geometry of the absorbed MLA attention (DeepSeek-V3 / Kimi style). */
+#define DDTREE_HEADS 64      /* query heads sharing one latent cache                    */
+#define DDTREE_D_LATENT 512  /* c_kv / q_lat width; also the value and output width     */
+#define DDTREE_D_ROPE 64     /* k_pe / q_pe width                                        */
+#define DDTREE_MAX_Q_LEN 64  /* tree nodes per stream (one 64-bit ancestor mask)         */
+
+/* Return codes. */
+#define DDTREE_OK 0
+#define DDTREE_ERR_NULL (-1)      /* a required pointer is NULL                               */
+#define DDTREE_ERR_SHAPE (-2)     /* a size is out of range                                   */
+#define DDTREE_ERR_ALIGN (-3)     /* a tensor pointer is not 16-byte aligned                  */
+#define DDTREE_ERR_ALIAS (-4)     /* an output range overlaps an input range                  */
+#define DDTREE_ERR_WORKSPACE (-5) /* workspace missing or smaller than the size query says     */
+#define DDTREE_ERR_HIP (-6)       /* the HIP runtime reported an error at launch              */
+
+/* Bits of the optional device status word. */
+#define DDTREE_STATUS_BAD_PARENTS 1 /* a parents[] entry is not an earlier node; that node's
+                                       ancestor walk stops there                               */
+#define DDTREE_STATUS_BAD_KEEP 2    /* keep[]/n_keep of a stream invalid; that stream untouched */
+
+/*
+ * ddtree_verify_attn -- tree-verify attention, absorbed MLA form, one launch for all streams.
+ *
+ * For every stream s, tree node i < q_len and head h < 64, with P = prefix_len, L = P + q_len:
+ *
+ *   visible(i)   = cache rows [0, P)  U  { P + j : j is i or an ancestor of i in parents[s] }
+ *   score(t)     = scale * ( q_lat[s,i,h,:] . ckv[s,t,:] + q_pe[s,i,h,:] . kpe[s,t,:] )
+ *   lse[s,i,h]   = ln( sum_{t in visible(i)} exp(score(t)) )
+ *   out_lat[s,i,h,:] = sum_{t in visible(i)} exp(score(t) - lse[s,i,h]) * ckv[s,t,:]
+ *
+ * with scale = 1/sqrt(192).  Row P + i of the cache holds tree node i, and every parent index
+ * is smaller than its child's (page above, section "The Cache Compaction Problem").
+ *
+ * Arguments (all device pointers, densely packed, 16-byte aligned):
+ *   q_lat    bf16  [n_streams][q_len][64][512]   per-head queries mapped into the latent space
+ *   q_pe     bf16  [n_streams][q_len][64][64]    rotary query part (already rotated)
+ *   ckv      bf16  [n_streams][prefix_len+q_len][512]  shared latent rows (keys and values)
+ *   kpe      bf16  [n_streams][prefix_len+q_len][64]   shared rotary key rows
+ *   parents  int32 [n_streams][q_len]            parents[s][0] = -1, else 0 <= p < node
+ *   out_lat  fp32  [n_streams][q_len][64][512]   written
+ *   lse      fp32  [n_streams][q_len][64]        written (natural log)
+ * Sizes: 0 <= prefix_len, 1 <= q_len <= 64, 1 <= n_streams.
+ * Errors: DDTREE_ERR_NULL / _SHAPE / _ALIGN / _ALIAS / _HIP.  No workspace: the whole key
+ * range of a (stream, query pair) is processed by one workgroup.
+ */
+int ddtree_verify_attn(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
+                       int prefix_len, const int32_t* parents, int q_len, int n_streams,
+                       float* out_lat, float* lse, hipStream_t stream);
+
+/*
+ * ddtree_verify_attn_ex -- as ddtree_verify_attn, plus:
+ *   kv_rows          per-stream row stride of ckv/kpe, >= prefix_len + q_len (rows past
+ *                    prefix_len + q_len are never read)
+ *   scale            softmax scale; <= 0 selects 1/sqrt(192)
+ *   num_splits       key-range splits per (stream, query pair): 0 = automatic (enough
+ *                    workgroups to fill the GPU), 1 = none, n > 1 = at most n.  Splits are
+ *                    merged by their log-sum-exp in a second kernel.
+ *   workspace        device scratch for split partials (may be NULL when the size query
+ *   workspace_bytes  returns 0 for these arguments)
+ *   dev_status       optional device int32 status word (may be NULL)
+ */
+int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
+                          int prefix_len, const int32_t* parents, int q_len, int n_streams,
+                          float* out_lat, float* lse, int kv_rows, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                          hipStream_t stream);
+
+/* Bytes of workspace ddtree_verify_attn_ex needs for these arguments (0 when no split is
+ * used).  Returns 0 for invalid sizes as well; the launch call then reports the error. */
+size_t ddtree_verify_attn_workspace_size(int prefix_len, int q_len, int n_streams,
+                                         int num_splits);
+
+/* The number of splits ddtree_verify_attn_ex will use for these arguments (>= 1), or a
+ * negative DDTREE_ERR_SHAPE for invalid sizes. */
+int ddtree_verify_attn_num_splits(int prefix_len, int q_len, int n_streams, int num_splits);
+
+/* The latent KV cache of n_streams streams: ckv bf16 [n_streams][kv_rows][512] and
+ * kpe bf16 [n_streams][kv_rows][64], one logical row = 576 bf16 values. */
+typedef struct ddtree_kv_cache {
+  void* ckv;
+  void* kpe;
+  int kv_rows;
+  int n_streams;
+} ddtree_kv_cache;
+
+/*
+ * ddtree_compact_kv -- post-accept KV compaction, in place and race-free.
+ *
+ * For every stream s with n = n_keep[s] and every i < n:
+ *   row prefix_len + i of ckv and kpe  <-  the ORIGINAL row prefix_len + keep[s][i]
+ * All other rows are left bit-identical.  keep[s] must be strictly increasing with
+ * keep[s][0] >= 0 and prefix_len + keep[s][n-1] < kv_rows (so keep[i] >= i: an accepted
+ * root-to-node path, page above, section "The Cache Compaction Problem").
+ * One workgroup per stream reads every kept row before any row is written, so the reader/
+ * writer race that section analyses cannot occur.  The copy is bitwise.
+ *
+ * Arguments:
+ *   cache        host pointer to the cache descriptor (device data pointers inside)
+ *   prefix_len   committed rows before the tree block, >= 0
+ *   keep         device int32 [n_streams][keep_stride], positions within the tree block
+ *   n_keep       device int32 [n_streams], each 0 <= n_keep[s] <= min(keep_stride, 64)
+ *   keep_stride  >= 1
+ *   dev_status   optional device int32 status word (DDTREE_STATUS_BAD_KEEP), may be NULL
+ * Errors: DDTREE_ERR_NULL / _SHAPE / _ALIGN / _HIP.  A stream whose keep/n_keep is invalid is
+ * skipped and flagged in dev_status.
+ */
+int ddtree_compact_kv(const ddtree_kv_cache* cache, int prefix_len, const int32_t* keep,
+                      const int32_t* n_keep, int keep_stride, int32_t* dev_status,
+                      hipStream_t stream);
+
+/* Static text for a return code. */
+const char* ddtree_status_string(int code);
+
+/* DDTREE_VERSION of the built library. */
+int ddtree_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDTREE_H */

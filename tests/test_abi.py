@@ -1,0 +1,126 @@
+"""The C-ABI library on the CPU: it loads, exports every function ``include/ddtree.h`` declares,
+and rejects invalid arguments with the documented codes before anything is launched.
+
+Every call here is built to fail host-side validation (the fake pointers are never
+dereferenced), so no kernel is ever launched from these tests.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tree_verify_mla_absorb_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ddtree.h")
+
+A = 0x10000  # fake, 16-byte aligned device addresses, far apart
+B = 0x20000000
+C = 0x40000000
+D = 0x60000000
+E = 0x80000000
+F = 0xA0000000
+G = 0xC0000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ddtree_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == sorted(_lib.EXPORTED), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert _lib.version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert _lib.status_string(code) not in ("", "unknown status")
+    assert _lib.status_string(-99) == "unknown status"
+
+
+def verify(q_lat=A, q_pe=B, ckv=C, kpe=D, prefix=100, parents=E, q=9, s=2, out=F, lse=G, rows=None, splits=1,
+           ws=None, ws_bytes=0, status=None, scale=0.0):
+    rows = prefix + q if rows is None else rows
+    return _lib.LIB.ddtree_verify_attn_ex(q_lat, q_pe, ckv, kpe, prefix, parents, q, s, out, lse, rows, scale,
+                                          splits, ws, ws_bytes, status, None)
+
+
+@pytest.mark.parametrize("field", ["q_lat", "q_pe", "ckv", "kpe", "parents", "out", "lse"])
+def test_null_pointers(field):
+    kw = {field: None}
+    assert verify(**kw) == _lib.ERR_NULL
+    assert verify(**kw, q=0) == _lib.ERR_NULL  # NULL is reported first
+
+
+@pytest.mark.parametrize("kw", [dict(q=0), dict(q=65), dict(s=0), dict(prefix=-1), dict(rows=50),
+                                dict(splits=-1)])
+def test_bad_shapes(kw):
+    assert verify(**kw) == _lib.ERR_SHAPE
+
+
+def test_plain_entry_rejects_shapes():
+    f = _lib.LIB.ddtree_verify_attn
+    assert f(A, B, C, D, 10, E, 65, 1, F, G, None) == _lib.ERR_SHAPE
+    assert f(A, B, C, D, 10, E, 9, 0, F, G, None) == _lib.ERR_SHAPE
+    assert f(None, B, C, D, 10, E, 9, 1, F, G, None) == _lib.ERR_NULL
+
+
+@pytest.mark.parametrize("field", ["q_lat", "q_pe", "ckv", "kpe", "out"])
+def test_misaligned(field):
+    base = {"q_lat": A, "q_pe": B, "ckv": C, "kpe": D, "out": F}[field]
+    assert verify(**{field: base + 8}) == _lib.ERR_ALIGN
+
+
+def test_aliasing_outputs():
+    assert verify(out=A) == _lib.ERR_ALIAS          # out over q_lat
+    assert verify(lse=C + 64) == _lib.ERR_ALIAS     # lse inside ckv
+    assert verify(lse=F + 1024) == _lib.ERR_ALIAS   # lse inside out
+
+
+def test_workspace_required_for_splits():
+    need = _lib.workspace_size(1000, 9, 2, 4)
+    assert _lib.num_splits(1000, 9, 2, 4) == 4
+    assert need == 4 * 2 * 9 * 64 * (512 + 1) * 4
+    assert verify(prefix=1000, splits=4) == _lib.ERR_WORKSPACE
+    assert verify(prefix=1000, splits=4, ws=0x100000000, ws_bytes=need - 4) == _lib.ERR_WORKSPACE
+    assert verify(prefix=1000, splits=4, ws=0x100000008, ws_bytes=need) == _lib.ERR_WORKSPACE  # misaligned
+    assert verify(prefix=1000, splits=4, ws=F, ws_bytes=need) == _lib.ERR_ALIAS  # workspace over out
+
+
+def test_split_queries():
+    assert _lib.workspace_size(100, 9, 1, 1) == 0
+    assert _lib.LIB.ddtree_verify_attn_workspace_size(100, 0, 1, 1) == 0
+    assert _lib.LIB.ddtree_verify_attn_num_splits(100, 65, 1, 1) == _lib.ERR_SHAPE
+    # splits never exceed the number of 64-key tiles and every split is non-empty
+    assert _lib.num_splits(0, 9, 1, 32) == 1
+    assert _lib.num_splits(100, 9, 1, 32) == 2
+    assert _lib.num_splits(4096, 33, 1, 13) == 13
+    assert _lib.num_splits(4096, 33, 1, 12) == 12 - 1  # 65 tiles: 6 per split -> 11 splits
+
+
+def compact(ckv=A, kpe=C, rows=300, s=2, prefix=100, keep=E, n_keep=F, stride=33, status=None, cache=True):
+    c = _lib.KVCache(ckv, kpe, rows, s)
+    return _lib.LIB.ddtree_compact_kv(ctypes.byref(c) if cache else None, prefix, keep, n_keep, stride, status,
+                                      None)
+
+
+def test_compact_argument_errors():
+    assert compact(cache=False) == _lib.ERR_NULL
+    assert compact(ckv=None) == _lib.ERR_NULL
+    assert compact(keep=None) == _lib.ERR_NULL
+    assert compact(n_keep=None) == _lib.ERR_NULL
+    assert compact(s=0) == _lib.ERR_SHAPE
+    assert compact(prefix=-1) == _lib.ERR_SHAPE
+    assert compact(prefix=301) == _lib.ERR_SHAPE
+    assert compact(stride=0) == _lib.ERR_SHAPE
+    assert compact(ckv=A + 8) == _lib.ERR_ALIGN
+    assert compact(keep=E + 2) == _lib.ERR_ALIGN
+    assert compact(kpe=A + 1024) == _lib.ERR_ALIAS

@@ -1,0 +1,183 @@
+"""Thin ctypes binding over ``libddtree.so`` (declared in ``include/ddtree.h``).
+
+Argument marshalling only: torch supplies device memory and the current HIP stream; every step
+of the computation runs in the library's gfx950 kernels.  There is no fallback: if the library
+is missing or fails to load, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libddtree.so")
+
+OK = 0
+ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = -1, -2, -3, -4, -5, -6
+STATUS_BAD_PARENTS, STATUS_BAD_KEEP = 1, 2
+HEADS, D_LATENT, D_ROPE, MAX_Q_LEN = 64, 512, 64, 64
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m tree_verify_mla_absorb_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.ddtree_verify_attn.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, vp]
+    lib.ddtree_verify_attn.restype = i32
+    lib.ddtree_verify_attn_ex.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, i32, f32, i32, vp, sz,
+                                          vp, vp]
+    lib.ddtree_verify_attn_ex.restype = i32
+    lib.ddtree_verify_attn_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.ddtree_verify_attn_workspace_size.restype = sz
+    lib.ddtree_verify_attn_num_splits.argtypes = [i32, i32, i32, i32]
+    lib.ddtree_verify_attn_num_splits.restype = i32
+    lib.ddtree_compact_kv.argtypes = [vp, i32, vp, vp, i32, vp, vp]
+    lib.ddtree_compact_kv.restype = i32
+    lib.ddtree_status_string.argtypes = [i32]
+    lib.ddtree_status_string.restype = ctypes.c_char_p
+    lib.ddtree_version.argtypes = []
+    lib.ddtree_version.restype = i32
+    return lib
+
+
+LIB = _load()
+
+EXPORTED = (
+    "ddtree_verify_attn",
+    "ddtree_verify_attn_ex",
+    "ddtree_verify_attn_workspace_size",
+    "ddtree_verify_attn_num_splits",
+    "ddtree_compact_kv",
+    "ddtree_status_string",
+    "ddtree_version",
+)
+
+
+class KVCache(ctypes.Structure):
+    """``ddtree_kv_cache``: device pointers plus the per-stream row count."""
+
+    _fields_ = [("ckv", ctypes.c_void_p), ("kpe", ctypes.c_void_p), ("kv_rows", ctypes.c_int),
+                ("n_streams", ctypes.c_int)]
+
+
+class DDTreeError(RuntimeError):
+    def __init__(self, code: int):
+        self.code = code
+        super().__init__(f"ddtree error {code}: {status_string(code)}")
+
+
+def status_string(code: int) -> str:
+    return LIB.ddtree_status_string(int(code)).decode()
+
+
+def version() -> int:
+    return int(LIB.ddtree_version())
+
+
+def _check(code: int) -> None:
+    if code != OK:
+        raise DDTreeError(code)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+_BF16 = (torch.bfloat16, torch.int16)
+
+
+def workspace_size(prefix_len: int, q_len: int, n_streams: int, num_splits: int = 0) -> int:
+    return int(LIB.ddtree_verify_attn_workspace_size(prefix_len, q_len, n_streams, num_splits))
+
+
+def num_splits(prefix_len: int, q_len: int, n_streams: int, num_splits: int = 0) -> int:
+    n = int(LIB.ddtree_verify_attn_num_splits(prefix_len, q_len, n_streams, num_splits))
+    _check(min(n, 0))
+    return n
+
+
+def _outputs(q_lat, out, lse):
+    s, q, h = q_lat.shape[0], q_lat.shape[1], q_lat.shape[2]
+    if out is None:
+        out = torch.empty((s, q, h, D_LATENT), dtype=torch.float32, device=q_lat.device)
+    if lse is None:
+        lse = torch.empty((s, q, h), dtype=torch.float32, device=q_lat.device)
+    _need(out, "out", (torch.float32,))
+    _need(lse, "lse", (torch.float32,))
+    return out, lse
+
+
+def _shapes(q_lat, q_pe, ckv, kpe, parents):
+    for t, n in ((q_lat, "q_lat"), (q_pe, "q_pe"), (ckv, "ckv"), (kpe, "kpe")):
+        _need(t, n, _BF16)
+    _need(parents, "parents", (torch.int32,))
+    s, q = parents.shape
+    if q_lat.shape != (s, q, HEADS, D_LATENT) or q_pe.shape != (s, q, HEADS, D_ROPE):
+        raise ValueError("q_lat / q_pe shape mismatch")
+    if ckv.shape[0] != s or ckv.shape[2] != D_LATENT or kpe.shape[:2] != ckv.shape[:2] or kpe.shape[2] != D_ROPE:
+        raise ValueError("ckv / kpe shape mismatch")
+    return s, q, ckv.shape[1]
+
+
+def verify_attn(q_lat, q_pe, ckv, kpe, prefix_len: int, parents, *, out=None, lse=None, stream=None):
+    """``ddtree_verify_attn``: one launch, no split, cache rows exactly ``prefix_len + q_len``."""
+    s, q, rows = _shapes(q_lat, q_pe, ckv, kpe, parents)
+    if rows != prefix_len + q:
+        raise ValueError("ckv must hold exactly prefix_len + q_len rows per stream (use verify_attn_ex)")
+    out, lse = _outputs(q_lat, out, lse)
+    _check(LIB.ddtree_verify_attn(_ptr(q_lat), _ptr(q_pe), _ptr(ckv), _ptr(kpe), int(prefix_len), _ptr(parents),
+                                  int(q), int(s), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def verify_attn_ex(q_lat, q_pe, ckv, kpe, prefix_len: int, parents, *, out=None, lse=None, scale: float = 0.0,
+                   num_splits: int = 0, workspace=None, status=None, stream=None):
+    """``ddtree_verify_attn_ex``.  ``workspace`` (uint8 device tensor) is allocated here when the
+    chosen split count needs one and none is given."""
+    s, q, rows = _shapes(q_lat, q_pe, ckv, kpe, parents)
+    out, lse = _outputs(q_lat, out, lse)
+    need = workspace_size(prefix_len, q, s, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if status is not None:
+        _need(status, "status", (torch.int32,))
+    _check(LIB.ddtree_verify_attn_ex(_ptr(q_lat), _ptr(q_pe), _ptr(ckv), _ptr(kpe), int(prefix_len), _ptr(parents),
+                                     int(q), int(s), _ptr(out), _ptr(lse), int(rows), float(scale),
+                                     int(num_splits), _ptr(workspace), nbytes, _ptr(status), _stream(stream)))
+    return out, lse
+
+
+def compact_kv(ckv, kpe, prefix_len: int, keep, n_keep, *, status=None, stream=None) -> None:
+    """``ddtree_compact_kv`` in place on ``ckv [S, rows, 512]`` / ``kpe [S, rows, 64]``."""
+    _need(ckv, "ckv", _BF16)
+    _need(kpe, "kpe", _BF16)
+    _need(keep, "keep", (torch.int32,))
+    _need(n_keep, "n_keep", (torch.int32,))
+    if status is not None:
+        _need(status, "status", (torch.int32,))
+    s, rows = ckv.shape[0], ckv.shape[1]
+    if kpe.shape[:2] != (s, rows) or keep.dim() != 2 or keep.shape[0] != s or n_keep.shape != (s,):
+        raise ValueError("shape mismatch")
+    cache = KVCache(ckv.data_ptr(), kpe.data_ptr(), int(rows), int(s))
+    _check(LIB.ddtree_compact_kv(ctypes.byref(cache), int(prefix_len), _ptr(keep), _ptr(n_keep), int(keep.shape[1]),
+                                 _ptr(status), _stream(stream)))
