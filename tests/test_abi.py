@@ -88,7 +88,13 @@ def test_aliasing_outputs():
 def test_workspace_required_for_splits():
     need = _lib.workspace_size(1000, 9, 2, 4)
     assert _lib.num_splits(1000, 9, 2, 4) == 4
-    assert need == 4 * 2 * 9 * 64 * (512 + 1) * 4
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+    # node pairs: 2 streams x 4 pairs x 128 rows; last node: 2 streams x 64 rows; 4 splits each
+    rows0, rows1 = 2 * 4 * 128, 2 * 64
+    assert need == (a256(4 * rows0 * 512 * 4) + a256(4 * rows1 * 512 * 4) + a256(4 * rows0 * 4)
+                    + a256(4 * rows1 * 4))
     assert verify(prefix=1000, splits=4) == _lib.ERR_WORKSPACE
     assert verify(prefix=1000, splits=4, ws=0x100000000, ws_bytes=need - 4) == _lib.ERR_WORKSPACE
     assert verify(prefix=1000, splits=4, ws=0x100000008, ws_bytes=need) == _lib.ERR_WORKSPACE  # misaligned

@@ -42,63 +42,114 @@ int cu_count() {
 }
 
 struct Plan {
-  int n_qgroups = 0;
+  int n_pairs = 0;     // node pairs per stream (group 0)
+  int has_odd = 0;     // 1 when q_len is odd (group 1: the last node alone)
   int n_tiles = 0;
-  int n_splits = 1;
-  int tiles_per_split = 0;
+  int splits[2] = {1, 1};
+  int tiles_per_split[2] = {0, 0};
+  long long wgs[2] = {0, 0};
+  long long part_rows[2] = {0, 0};
 };
 
 bool shape_ok(int prefix_len, int q_len, int n_streams) {
+  // kv rows are addressed with 32-bit byte offsets inside one stream's cache
   return prefix_len >= 0 && q_len >= 1 && q_len <= kMaxQ && n_streams >= 1 &&
-         (long long)prefix_len + q_len <= 0x7fffffffLL - kTileKeys;
+         (long long)prefix_len + q_len <= (1LL << 21);
 }
 
-// Key-range split count.  Each (stream, query pair) unit walks n_tiles key tiles; splitting
-// lets small launches fill the GPU at the price of a merge pass over fp32 partials.  The
-// automatic choice minimises a simple time model: rounds of workgroups over the CUs times
-// tiles per workgroup, plus the partial traffic of the merge expressed in tile-times.
-Plan make_plan(int prefix_len, int q_len, int n_streams, int num_splits) {
-  Plan p;
-  p.n_qgroups = (q_len + kQueriesPerWG - 1) / kQueriesPerWG;
-  p.n_tiles = (prefix_len + q_len + kTileKeys - 1) / kTileKeys;
-  const long long units = (long long)n_streams * p.n_qgroups;
-  int want;
-  if (num_splits > 0) {
-    want = num_splits;
-  } else {
-    const int cus = cu_count();
-    // One tile of one unit is ~17.8 MFLOP, ~2.2 us on one CU.  Each (unit, split) partial
-    // costs 0.5 MB of HBM traffic (128 rows x 2 KiB written, then read by the merge), ~64 ns
-    // of the whole GPU's bandwidth: ~0.03 tile-times.  Plus a fixed cost for the second launch.
-    double best = 1e300;
-    want = 1;
-    for (int sp = 1; sp <= kMaxSplits && sp <= p.n_tiles; ++sp) {
-      const int tps = (p.n_tiles + sp - 1) / sp;
-      const int eff = (p.n_tiles + tps - 1) / tps;
-      const double rounds = ceil((double)units * eff / cus);
-      const double merge = eff > 1 ? 0.03 * (double)units * eff + 0.5 : 0.0;
-      const double cost = rounds * tps + merge;
-      if (cost < best - 1e-9) {
-        best = cost;
-        want = sp;
-      }
-    }
-  }
+// Normalise a requested split count: every split gets the same number of tiles and none is
+// empty.
+void set_splits(Plan& p, int g, int want) {
   if (want > kMaxSplits) want = kMaxSplits;
   if (want > p.n_tiles) want = p.n_tiles;
   if (want < 1) want = 1;
-  p.tiles_per_split = (p.n_tiles + want - 1) / want;
-  p.n_splits = (p.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;  // every split non-empty
+  p.tiles_per_split[g] = (p.n_tiles + want - 1) / want;
+  p.splits[g] = (p.n_tiles + p.tiles_per_split[g] - 1) / p.tiles_per_split[g];
+}
+
+// Estimated time of a plan, in units of one workgroup-tile (64 keys x 128 query-heads, about
+// 18 MFLOP, ~2-3 us on one CU).  Workgroups of group 0 are dispatched first, then group 1's,
+// each to the next free CU.  When group 0 fills whole rounds, group 1 runs in rounds of its own
+// after it; otherwise the estimate is the larger of group 0's own rounds and the
+// list-scheduling bound (total work / CUs + one group-1 workgroup).  A split group pays for its
+// partials: 2 KiB per row written and read back by the merge (~0.03 tile-times per 128 rows of
+// one split on the whole GPU's bandwidth) plus a fixed cost for the merge launch.
+double plan_cost(const Plan& p, long long units0, long long units1, int cus) {
+  const double c0 = p.tiles_per_split[0], c1 = p.tiles_per_split[1];
+  const long long n0 = units0 * p.splits[0], n1 = units1 * p.splits[1];
+  const double end0 = n0 ? (double)((n0 + cus - 1) / cus) * c0 : 0.0;
+  double t = end0;
+  if (n1) {
+    if (n0 % cus == 0)
+      t = end0 + (double)((n1 + cus - 1) / cus) * c1;
+    else
+      t = fmax(end0, ((double)n0 * c0 + (double)n1 * c1) / cus + c1);
+  }
+  if (n0 && p.splits[0] > 1) t += 0.03 * (double)n0 + 0.5;
+  if (n1 && p.splits[1] > 1) t += 0.015 * (double)n1 + 0.5;
+  return t;
+}
+
+Plan make_plan(int prefix_len, int q_len, int n_streams, int num_splits) {
+  Plan p;
+  p.n_pairs = q_len / 2;
+  p.has_odd = q_len & 1;
+  p.n_tiles = (prefix_len + q_len + kTileKeys - 1) / kTileKeys;
+  const long long units0 = (long long)n_streams * p.n_pairs;
+  const long long units1 = (long long)n_streams * p.has_odd;
+  if (num_splits > 0) {
+    set_splits(p, 0, num_splits);
+    set_splits(p, 1, num_splits);
+  } else {
+    const int cus = cu_count();
+    double best = 1e300;
+    Plan trial = p;
+    for (int s0 = 1; s0 <= 16 && s0 <= p.n_tiles; ++s0) {
+      if (units0 == 0 && s0 > 1) break;
+      set_splits(trial, 0, s0);
+      if (trial.splits[0] != s0) continue;
+      for (int s1 = 1; s1 <= kMaxSplits && s1 <= p.n_tiles; s1 *= 2) {
+        if (units1 == 0 && s1 > 1) break;
+        set_splits(trial, 1, s1);
+        const double c = plan_cost(trial, units0, units1, cus);
+        if (c < best - 1e-9) {
+          best = c;
+          p.splits[0] = trial.splits[0];
+          p.tiles_per_split[0] = trial.tiles_per_split[0];
+          p.splits[1] = trial.splits[1];
+          p.tiles_per_split[1] = trial.tiles_per_split[1];
+        }
+      }
+    }
+  }
+  if (p.tiles_per_split[0] == 0) set_splits(p, 0, 1);
+  if (p.tiles_per_split[1] == 0) set_splits(p, 1, 1);
+  p.wgs[0] = units0 * p.splits[0];
+  p.wgs[1] = units1 * p.splits[1];
+  p.part_rows[0] = units0 * 2 * kHeads;
+  p.part_rows[1] = units1 * kHeads;
   return p;
 }
 
-size_t part_out_bytes(const Plan& p, int q_len, int n_streams) {
-  return (size_t)p.n_splits * n_streams * q_len * kHeads * kDLat * sizeof(float);
+// Workspace: [group 0 out partials][group 1 out partials][group 0 lse][group 1 lse], each part
+// present only when its group is split, every part 256-byte aligned.
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t part_out_bytes(const Plan& p, int g) {
+  return p.splits[g] > 1 && p.wgs[g] ? align256((size_t)p.splits[g] * p.part_rows[g] * kDLat * sizeof(float)) : 0;
 }
-size_t workspace_bytes_for(const Plan& p, int q_len, int n_streams) {
-  if (p.n_splits <= 1) return 0;
-  const size_t lse_bytes = (size_t)p.n_splits * n_streams * q_len * kHeads * sizeof(float);
-  return part_out_bytes(p, q_len, n_streams) + lse_bytes;
+size_t part_lse_bytes(const Plan& p, int g) {
+  return p.splits[g] > 1 && p.wgs[g] ? align256((size_t)p.splits[g] * p.part_rows[g] * sizeof(float)) : 0;
+}
+size_t workspace_bytes_for(const Plan& p) {
+  return part_out_bytes(p, 0) + part_out_bytes(p, 1) + part_lse_bytes(p, 0) + part_lse_bytes(p, 1);
+}
+
+// Split count reported to callers: the larger of the two groups'.
+int reported_splits(const Plan& p) {
+  int n = 1;
+  for (int g = 0; g < 2; ++g)
+    if (p.wgs[g] && p.splits[g] > n) n = p.splits[g];
+  return n;
 }
 
 }  // namespace
@@ -122,13 +173,12 @@ const char* ddtree_status_string(int code) {
 
 int ddtree_verify_attn_num_splits(int prefix_len, int q_len, int n_streams, int num_splits) {
   if (!shape_ok(prefix_len, q_len, n_streams) || num_splits < 0) return DDTREE_ERR_SHAPE;
-  return make_plan(prefix_len, q_len, n_streams, num_splits).n_splits;
+  return reported_splits(make_plan(prefix_len, q_len, n_streams, num_splits));
 }
 
 size_t ddtree_verify_attn_workspace_size(int prefix_len, int q_len, int n_streams, int num_splits) {
   if (!shape_ok(prefix_len, q_len, n_streams) || num_splits < 0) return 0;
-  const Plan p = make_plan(prefix_len, q_len, n_streams, num_splits);
-  return workspace_bytes_for(p, q_len, n_streams);
+  return workspace_bytes_for(make_plan(prefix_len, q_len, n_streams, num_splits));
 }
 
 int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
@@ -142,6 +192,7 @@ int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, 
   if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(ckv) || !aligned16(kpe) || !aligned16(out_lat) ||
       !aligned4(lse) || !aligned4(parents) || (dev_status && !aligned4(dev_status)))
     return DDTREE_ERR_ALIGN;
+  if (kv_rows > (1 << 21)) return DDTREE_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) scale = 1.0f / sqrtf(192.0f);
 
   const size_t rows_q = (size_t)n_streams * q_len * kHeads;
@@ -157,7 +208,7 @@ int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, 
   if (overlap(r_out, r_lse)) return DDTREE_ERR_ALIAS;
 
   const Plan plan = make_plan(prefix_len, q_len, n_streams, num_splits);
-  const long long blocks = (long long)n_streams * plan.n_qgroups * plan.n_splits;
+  const long long blocks = plan.wgs[0] + plan.wgs[1];
   if (blocks > kMaxGrid) return DDTREE_ERR_SHAPE;
 
   ddtree::VerifyArgs a{};
@@ -166,42 +217,52 @@ int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, 
   a.ckv = static_cast<const uint16_t*>(ckv);
   a.kpe = static_cast<const uint16_t*>(kpe);
   a.parents = parents;
+  a.out = out_lat;
+  a.lse = lse;
   a.status = dev_status;
   a.prefix_len = prefix_len;
   a.q_len = q_len;
   a.n_streams = n_streams;
   a.kv_rows = kv_rows;
-  a.n_qgroups = plan.n_qgroups;
-  a.n_splits = plan.n_splits;
-  a.tiles_per_split = plan.tiles_per_split;
+  a.n_pairs = plan.n_pairs;
   a.n_tiles = plan.n_tiles;
+  for (int g = 0; g < 2; ++g) {
+    a.splits[g] = plan.splits[g];
+    a.tiles_per_split[g] = plan.tiles_per_split[g];
+  }
+  a.wg_count0 = (int)plan.wgs[0];
   a.scale_log2e = scale * 1.4426950408889634f;
 
-  if (plan.n_splits > 1) {
-    const size_t need = workspace_bytes_for(plan, q_len, n_streams);
+  const size_t need = workspace_bytes_for(plan);
+  if (need > 0) {
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DDTREE_ERR_WORKSPACE;
     const Range r_ws = range_of(workspace, need);
     for (const Range& in : inputs)
       if (overlap(in, r_ws)) return DDTREE_ERR_ALIAS;
     if (overlap(r_ws, r_out) || overlap(r_ws, r_lse)) return DDTREE_ERR_ALIAS;
-    a.part_out = static_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_out_bytes(plan, q_len, n_streams));
-    a.out = nullptr;
-    a.lse = nullptr;
-  } else {
-    a.out = out_lat;
-    a.lse = lse;
+    char* w = static_cast<char*>(workspace);
+    for (int g = 0; g < 2; ++g) {
+      a.part_out[g] = part_out_bytes(plan, g) ? reinterpret_cast<float*>(w) : nullptr;
+      w += part_out_bytes(plan, g);
+    }
+    for (int g = 0; g < 2; ++g) {
+      a.part_lse[g] = part_lse_bytes(plan, g) ? reinterpret_cast<float*>(w) : nullptr;
+      w += part_lse_bytes(plan, g);
+    }
   }
-  if (ddtree::launch_verify(a, stream) != hipSuccess) return DDTREE_ERR_HIP;
-  if (plan.n_splits > 1) {
+  if (ddtree::launch_verify(a, (int)blocks, stream) != hipSuccess) return DDTREE_ERR_HIP;
+  for (int g = 0; g < 2; ++g) {
+    if (!a.part_out[g]) continue;
     ddtree::CombineArgs c{};
-    c.part_out = a.part_out;
-    c.part_lse = a.part_lse;
+    c.part_out = a.part_out[g];
+    c.part_lse = a.part_lse[g];
     c.out = out_lat;
     c.lse = lse;
-    c.rows = (int)rows_q;
-    c.n_splits = plan.n_splits;
-    if ((long long)rows_q * 128 / 256 + 1 > kMaxGrid) return DDTREE_ERR_SHAPE;
+    c.rows = (int)plan.part_rows[g];
+    c.n_splits = plan.splits[g];
+    c.group = g;
+    c.n_pairs = plan.n_pairs;
+    c.q_len = q_len;
     if (ddtree::launch_combine(c, stream) != hipSuccess) return DDTREE_ERR_HIP;
   }
   return DDTREE_OK;

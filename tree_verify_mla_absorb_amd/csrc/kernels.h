@@ -11,43 +11,52 @@ constexpr int kDLat = 512;
 constexpr int kDRope = 64;
 constexpr int kMaxQ = 64;
 
-// verify_attn tiling: one workgroup = 4 waves = 2 tree queries x 64 heads; keys are staged
-// into LDS 64 rows at a time.
+// verify_attn tiling: one workgroup = 4 waves = 2 tree nodes x 64 heads; keys are staged into
+// LDS 64 rows at a time.
 constexpr int kQueriesPerWG = 2;
 constexpr int kTileKeys = 64;
 constexpr int kWGThreads = 256;
 
+// The launch holds two groups of workgroups.  Group 0: node pairs (2p, 2p + 1), p < q_len / 2.
+// Group 1 (odd q_len only): the last node alone.  Each group has its own key-range split count;
+// a group with more than one split writes (out, lse) partials that a merge pass combines.
+//   group 0 partial rows: ((s * n_pairs + p) * 2 + node_in_pair) * 64 + head
+//   group 1 partial rows: s * 64 + head
 struct VerifyArgs {
   const uint16_t* q_lat;
   const uint16_t* q_pe;
   const uint16_t* ckv;
   const uint16_t* kpe;
   const int32_t* parents;
-  float* out;          // final output (no split) -- or nullptr when partials are written
+  float* out;
   float* lse;
-  float* part_out;     // [splits][S][Q][64][512] (split > 1)
-  float* part_lse;     // [splits][S][Q][64]
+  float* part_out[2];  // [splits][rows of the group][512] when that group is split
+  float* part_lse[2];  // [splits][rows of the group]
   int32_t* status;
   int prefix_len;
   int q_len;
   int n_streams;
   int kv_rows;
-  int n_qgroups;       // ceil(q_len / 2)
-  int n_splits;
-  int tiles_per_split;
+  int n_pairs;         // q_len / 2
   int n_tiles;         // ceil((prefix_len + q_len) / 64)
+  int splits[2];
+  int tiles_per_split[2];
+  int wg_count0;       // workgroups of group 0; group 1 follows
   float scale_log2e;   // softmax scale * log2(e)
 };
 
-hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+hipError_t launch_verify(const VerifyArgs& a, int wg_total, hipStream_t stream);
 
 struct CombineArgs {
   const float* part_out;
   const float* part_lse;
   float* out;
   float* lse;
-  int rows;            // S * Q * 64
+  int rows;            // partial rows of the group
   int n_splits;
+  int group;           // 0 or 1 (row numbering above)
+  int n_pairs;
+  int q_len;
 };
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);

@@ -128,25 +128,33 @@ verify_attn_kernel(VerifyArgs a) {
   const int c32 = lane & 31;
   const int g = lane >> 5;
 
-  // Workgroup b is dispatched to XCD b % 8.  Renumber so that each XCD runs a contiguous run
-  // of (stream, query group, split) units: the workgroups of one stream then share that XCD's
-  // L2 while they stream the same key tiles.
-  const int nblk = gridDim.x;
-  const int xcd = blockIdx.x & 7;
-  const int per = nblk >> 3, rem = nblk & 7;
-  const int logical = xcd * per + min(xcd, rem) + (blockIdx.x >> 3);
-  const int sp = logical % a.n_splits;
-  const int unit = logical / a.n_splits;
-  const int s = unit / a.n_qgroups;
-  const int qg = unit - s * a.n_qgroups;
+  // Group and position of this workgroup.  Workgroup b is dispatched to XCD b % 8; within a
+  // group the index is renumbered so that each XCD runs a contiguous run of (stream, node pair,
+  // split) units: the workgroups of one stream then share that XCD's L2 while they stream the
+  // same key tiles, and the light workgroups of group 1 spread over all XCDs.
+  const int grp = (int)blockIdx.x < a.wg_count0 ? 0 : 1;
+  const int j = grp == 0 ? (int)blockIdx.x : (int)blockIdx.x - a.wg_count0;
+  const int cnt = grp == 0 ? a.wg_count0 : (int)gridDim.x - a.wg_count0;
+  const int xcd = j & 7;
+  const int per = cnt >> 3, rem = cnt & 7;
+  const int logical = xcd * per + min(xcd, rem) + (j >> 3);
+  const int n_split = a.splits[grp];
+  const int sp = logical % n_split;
+  const int unit = logical / n_split;
+  const int s = grp == 0 ? unit / max(a.n_pairs, 1) : unit;
+  const int pair = grp == 0 ? unit - s * a.n_pairs : 0;
+  const int q0 = grp == 0 ? 2 * pair : a.q_len - 1;  // first node of the workgroup
+  const int n_nodes = grp == 0 ? 2 : 1;
 
   const int P = a.prefix_len;
   const int Q = a.q_len;
   const int L = P + Q;
-  const int qi = qg * kQueriesPerWG + (wave >> 1);
-  const bool active = qi < Q;  // an idle head block (odd q_len) computes a copy of node Q-1
-  const int qc = active ? qi : Q - 1;
+  const int qi = q0 + (wave >> 1);
+  const bool active = (wave >> 1) < n_nodes;  // group 1: head blocks 2, 3 compute a copy
+  const int qc = active ? qi : q0;
   const int head = (wave & 1) * 32 + c32;
+  // row of (node q0 + k, head h) in this group's partial buffers
+  auto part_row = [&](int k, int h) { return grp == 0 ? ((s * a.n_pairs + pair) * 2 + k) * kHeads + h : s * kHeads + h; };
 
   // Ancestor-or-self mask of node qc.  Every step must move to a strictly smaller index, so
   // the walk ends within q_len steps for any input; a malformed entry ends it early.
@@ -235,8 +243,8 @@ verify_attn_kernel(VerifyArgs a) {
   float l_run = 0.f;     // this lane's share of the denominator
   float mx_run = -INFINITY;
   const float cs = a.scale_log2e;
-  const int t_begin = sp * a.tiles_per_split;
-  const int t_end = min(a.n_tiles, t_begin + a.tiles_per_split);
+  const int t_begin = sp * a.tiles_per_split[grp];
+  const int t_end = min(a.n_tiles, t_begin + a.tiles_per_split[grp]);
   const int t_mask = max(t_begin, min(t_end, P / kTileKeys));  // first tile holding tree keys
 
   // One 64-key tile held in stage `stg`: scores, probabilities, publish, values.
@@ -389,24 +397,23 @@ verify_attn_kernel(VerifyArgs a) {
   const float lt = half_sum(l_run);
   float* l_sh = reinterpret_cast<float*>(smem + kPOff);  // the P buffer is free after the last barrier
   if (g == 0) l_sh[wave * 32 + c32] = lt;
+  const int part_rows = grp == 0 ? a.n_streams * a.n_pairs * 2 * kHeads : a.n_streams * kHeads;
   if (active && g == 0) {
     const float lse_v = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY;
-    const size_t orow = ((size_t)s * Q + qi) * kHeads + head;
-    if (a.n_splits == 1)
-      a.lse[orow] = lse_v;
+    if (n_split == 1)
+      a.lse[((size_t)s * Q + qi) * kHeads + head] = lse_v;
     else
-      a.part_lse[(size_t)sp * a.n_streams * Q * kHeads + orow] = lse_v;
+      a.part_lse[grp][(size_t)sp * part_rows + part_row(wave >> 1, head)] = lse_v;
   }
   __syncthreads();
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
-    const int q_hb = qg * kQueriesPerWG + (hb >> 1);
-    if (q_hb >= Q) continue;
+    if ((hb >> 1) >= n_nodes) continue;
     const float lh = l_sh[hb * 32 + c32];
     const float inv = lh > 0.f ? 1.0f / lh : 0.f;
-    const size_t orow = ((size_t)s * Q + q_hb) * kHeads + (hb & 1) * 32 + c32;
-    float* dst = a.n_splits == 1 ? a.out + orow * kDLat
-                                 : a.part_out + ((size_t)sp * a.n_streams * Q * kHeads + orow) * kDLat;
+    const int h = (hb & 1) * 32 + c32;
+    float* dst = n_split == 1 ? a.out + (((size_t)s * Q + q0 + (hb >> 1)) * kHeads + h) * kDLat
+                              : a.part_out[grp] + ((size_t)sp * part_rows + part_row(hb >> 1, h)) * kDLat;
     dst += wave * 128 + 4 * g;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -424,12 +431,23 @@ verify_attn_kernel(VerifyArgs a) {
 }
 
 // Merge of key-range splits by log-sum-exp: lse = log sum_k exp(lse_k),
-// out = sum_k exp(lse_k - lse) out_k.  One thread per (row, 4 dims).
+// out = sum_k exp(lse_k - lse) out_k.  One thread per (partial row, 4 dims).
 __global__ void __launch_bounds__(256) verify_combine_kernel(CombineArgs a) {
   const int tid = blockIdx.x * blockDim.x + threadIdx.x;
   const int row = tid >> 7;
   const int c4 = tid & 127;
   if (row >= a.rows) return;
+  int orow;
+  if (a.group == 0) {
+    const int h = row & (kHeads - 1);
+    const int k = (row >> 6) & 1;
+    const int sp_pair = row >> 7;  // s * n_pairs + p
+    const int s = sp_pair / max(a.n_pairs, 1);
+    const int p = sp_pair - s * a.n_pairs;
+    orow = (s * a.q_len + 2 * p + k) * kHeads + h;
+  } else {
+    orow = ((row >> 6) * a.q_len + a.q_len - 1) * kHeads + (row & (kHeads - 1));
+  }
   float mx = -INFINITY;
   for (int k = 0; k < a.n_splits; ++k) mx = fmaxf(mx, a.part_lse[(size_t)k * a.rows + row]);
   float den = 0.f;
@@ -449,16 +467,15 @@ __global__ void __launch_bounds__(256) verify_combine_kernel(CombineArgs a) {
   acc.y *= inv;
   acc.z *= inv;
   acc.w *= inv;
-  *reinterpret_cast<float4*>(a.out + (size_t)row * kDLat + 4 * c4) = acc;
-  if (c4 == 0) a.lse[row] = mx + logf(den);
+  *reinterpret_cast<float4*>(a.out + (size_t)orow * kDLat + 4 * c4) = acc;
+  if (c4 == 0) a.lse[orow] = mx + logf(den);
 }
 
 }  // namespace
 
-hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
-  const long long blocks = (long long)a.n_streams * a.n_qgroups * a.n_splits;
+hipError_t launch_verify(const VerifyArgs& a, int wg_total, hipStream_t stream) {
   void* args[] = {const_cast<VerifyArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(verify_attn_kernel), dim3((unsigned)blocks),
+  return hipLaunchKernel(reinterpret_cast<const void*>(verify_attn_kernel), dim3((unsigned)wg_total),
                          dim3(kWGThreads), args, 0, stream);
 }
 
