@@ -89,6 +89,63 @@ def cpu_baseline(w, flops_per_stream: float, budget_s: float = 12.0):
                       f"({t_total:.1f} s)"}
 
 
+def _db_rows(path: str, sql: str):
+    import sqlite3
+    con = sqlite3.connect(path)
+    try:
+        return list(con.execute(sql))
+    finally:
+        con.close()
+
+
+def summarize_trace(db: str, command: str, skip: int = 0) -> str:
+    """Per-kernel dispatch statistics of a ``rocprofv3 --kernel-trace`` database, as text.
+    ``avg_timed_us`` leaves out each kernel's first ``skip`` dispatches (the warm-up steps)."""
+    rows = _db_rows(db, "select name, start, duration from kernels order by start")
+    per = {}
+    for name, _, dur in rows:
+        per.setdefault(name, []).append(dur / 1e3)
+    lines = [f"command: {command}", "units: microseconds per dispatch (trace durations in ns / 1000)",
+             f"kernel_source_sha256: {kernel_sha()}", f"warm-up dispatches left out of avg_timed_us: {skip}", "",
+             f"{'kernel':66s} {'calls':>5s} {'avg_us':>9s} {'avg_timed_us':>12s} {'min_us':>9s} {'max_us':>9s}"]
+    for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        short = name if len(name) <= 66 else name[:63] + "..."
+        timed = d[skip:] if len(d) > skip else d
+        lines.append(f"{short:66s} {len(d):5d} {sum(d) / len(d):9.2f} {sum(timed) / len(timed):12.2f} "
+                     f"{min(d):9.2f} {max(d):9.2f}")
+    return "\n".join(lines) + "\n"
+
+
+def _pmc_mean(db: str, kernel_substr: str, counter: str) -> float:
+    rows = _db_rows(db, "select name, counter_name, counter_value from pmc_events")
+    vals = [v for name, cn, v in rows if kernel_substr in name and cn == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} samples for {kernel_substr} in {db}")
+    return sum(vals) / len(vals)
+
+
+def summarize_pmc(fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_db: str, copy_bytes: int,
+                  commands: str) -> str:
+    """HBM bytes per verify launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled
+    by what the same counter reads for a plain device copy of ``copy_bytes``."""
+    copy_kernel = "copyBuffer"
+    cf = _pmc_mean(copy_fetch_db, copy_kernel, "FETCH_SIZE") * 1024.0
+    cw = _pmc_mean(copy_write_db, copy_kernel, "WRITE_SIZE") * 1024.0
+    f_scale, w_scale = copy_bytes / cf, copy_bytes / cw
+    kf = _pmc_mean(fetch_db, "verify_attn_kernel", "FETCH_SIZE") * 1024.0
+    kw = _pmc_mean(write_db, "verify_attn_kernel", "WRITE_SIZE") * 1024.0
+    total = kf * f_scale + kw * w_scale
+    lines = [f"commands: {commands}",
+             f"kernel_source_sha256: {kernel_sha()}",
+             f"copy_bytes: {copy_bytes}",
+             f"copy_fetch_size_bytes: {cf:.0f}  -> fetch scale {f_scale:.4f}",
+             f"copy_write_size_bytes: {cw:.0f}  -> write scale {w_scale:.4f}",
+             f"verify_fetch_size_bytes_raw: {kf:.0f}  scaled: {kf * f_scale:.0f}",
+             f"verify_write_size_bytes_raw: {kw:.0f}  scaled: {kw * w_scale:.0f}",
+             f"hbm_bytes_per_launch: {total:.0f}"]
+    return "\n".join(lines) + "\n"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,13 +154,40 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES, 3 times (for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("DB", "COMMAND", "SKIP"),
+                    help="print a per-kernel summary of a rocprofv3 kernel-trace database and exit")
+    ap.add_argument("--summarize-pmc", nargs=6,
+                    metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB", "COPY_BYTES", "COMMANDS"),
+                    help="print HBM bytes per verify launch from FETCH_SIZE / WRITE_SIZE runs and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        db, cmd, skip = args.summarize_trace
+        print(summarize_trace(db, cmd, int(skip)), end="")
+        return 0
+    if args.summarize_pmc:
+        f, w, cf, cw, nbytes, cmds = args.summarize_pmc
+        print(summarize_pmc(f, w, cf, cw, int(nbytes), cmds), end="")
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
                                    "(streams shard across GPUs with no communication; see DESIGN.md)"}))
         return 2
 
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 3}), flush=True)
+        return 0
 
     import synth
     from tree_verify_mla_absorb_amd import _lib
