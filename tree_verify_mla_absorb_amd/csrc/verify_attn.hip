@@ -326,37 +326,52 @@ verify_attn_kernel(VerifyArgs a) {
     __syncthreads();  // all four head blocks' probabilities published; rotary rows consumed
     if (prefetch) load_rope(t + 1);
 
-    // ---- O^T += V^T P^T: 4 slices of 16 keys, 4 dim blocks x 4 head blocks per slice
+    // ---- O^T += V^T P^T: 4 slices of 16 keys, 4 dim blocks x 4 head blocks per slice.
+    //      Step k = (slice, dim block); the reads of step k + 1 are issued before the MFMAs of
+    //      step k so that LDS latency overlaps the matrix work.
+    auto vfrag = [&](int k) __attribute__((always_inline)) -> bf16x8 {
+      const int sl = k >> 2, db = k & 3;
+      const unsigned char* vp = lat + tr_off + ((sl >> 1) * 32 + (sl & 1) * 16) * kRowStride + db * 64;
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 2 * kRowStride));
+      return __builtin_bit_cast(bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+    };
+    bf16x8 pf[4];
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      const int jt = sl >> 1, u = sl & 1;
-      bf16x8 pf[4];
+    for (int hb = 0; hb < 4; ++hb) pf[hb] = *reinterpret_cast<const bf16x8*>(p_all + hb * 4096);
+    bf16x8 vf = vfrag(0);
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb) pf[hb] = *reinterpret_cast<const bf16x8*>(p_all + hb * 4096 + sl * 1024);
-      const unsigned char* vp = lat + tr_off + (jt * 32 + u * 16) * kRowStride;
+    for (int k = 0; k < 16; ++k) {
+      const int sl = k >> 2, db = k & 3;
+      const bf16x8 vcur = vf;
+      bf16x8 pcur[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + db * 64));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 2 * kRowStride + db * 64));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+      for (int hb = 0; hb < 4; ++hb) pcur[hb] = pf[hb];
+      if (k + 1 < 16) {
+        vf = vfrag(k + 1);
+        if (((k + 1) & 3) == 0) {
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-          o[hb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[hb], o[hb][db], 0, 0, 0);
+          for (int hb = 0; hb < 4; ++hb)
+            pf[hb] = *reinterpret_cast<const bf16x8*>(p_all + hb * 4096 + ((k + 1) >> 2) * 1024);
+        }
       }
+      (void)sl;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        o[hb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, pcur[hb], o[hb][db], 0, 0, 0);
     }
     // Schedule: the reads of step k + 1 (two V^T halves, plus the next slice's four P^T
-    // fragments at a slice boundary) are issued after the first MFMA of step k.
+    // fragments at a slice boundary) are issued before the MFMAs of step k.
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 1);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
       if (k < 15) {
         if (((k + 1) & 3) == 0)
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 1);
         else
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3, 1);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
     }
   };
 
