@@ -105,11 +105,11 @@ def test_split_queries():
     assert _lib.workspace_size(100, 9, 1, 1) == 0
     assert _lib.LIB.ddtree_verify_attn_workspace_size(100, 0, 1, 1) == 0
     assert _lib.LIB.ddtree_verify_attn_num_splits(100, 65, 1, 1) == _lib.ERR_SHAPE
-    # splits never exceed the number of 64-key tiles and every split is non-empty
-    assert _lib.num_splits(0, 9, 1, 32) == 1
-    assert _lib.num_splits(100, 9, 1, 32) == 2
-    assert _lib.num_splits(4096, 33, 1, 13) == 13
-    assert _lib.num_splits(4096, 33, 1, 12) == 12 - 1  # 65 tiles: 6 per split -> 11 splits
+    # splits never exceed the number of 32-key tiles and every split is non-empty
+    assert _lib.num_splits(0, 9, 1, 32) == 1          # 9 keys: one tile
+    assert _lib.num_splits(100, 9, 1, 32) == 4        # 109 keys: four tiles
+    assert _lib.num_splits(4096, 33, 1, 13) == 13     # 130 tiles: 10 per split
+    assert _lib.num_splits(4096, 33, 1, 40) == 33     # 130 tiles: 4 per split -> 33 splits
 
 
 def compact(ckv=A, kpe=C, rows=300, s=2, prefix=100, keep=E, n_keep=F, stride=33, status=None, cache=True):

@@ -18,7 +18,7 @@ using ddtree::kMaxQ;
 using ddtree::kQueriesPerWG;
 using ddtree::kTileKeys;
 
-constexpr int kMaxSplits = 32;
+constexpr int kMaxSplits = 64;
 constexpr long long kMaxGrid = 0x7fffffffLL;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -67,12 +67,12 @@ void set_splits(Plan& p, int g, int want) {
   p.splits[g] = (p.n_tiles + p.tiles_per_split[g] - 1) / p.tiles_per_split[g];
 }
 
-// Estimated time of a plan, in units of one workgroup-tile (64 keys x 128 query-heads, about
-// 18 MFLOP, ~2-3 us on one CU).  Workgroups of group 0 are dispatched first, then group 1's,
+// Estimated time of a plan, in units of one workgroup-tile (32 keys x 128 query-heads, about
+// 9 MFLOP, ~1-1.5 us on one CU).  Workgroups of group 0 are dispatched first, then group 1's,
 // each to the next free CU.  When group 0 fills whole rounds, group 1 runs in rounds of its own
 // after it; otherwise the estimate is the larger of group 0's own rounds and the
 // list-scheduling bound (total work / CUs + one group-1 workgroup).  A split group pays for its
-// partials: 2 KiB per row written and read back by the merge (~0.03 tile-times per 128 rows of
+// partials: 2 KiB per row written and read back by the merge (~0.06 tile-times per 128 rows of
 // one split on the whole GPU's bandwidth) plus a fixed cost for the merge launch.
 double plan_cost(const Plan& p, long long units0, long long units1, int cus) {
   const double c0 = p.tiles_per_split[0], c1 = p.tiles_per_split[1];
@@ -85,8 +85,8 @@ double plan_cost(const Plan& p, long long units0, long long units1, int cus) {
     else
       t = fmax(end0, ((double)n0 * c0 + (double)n1 * c1) / cus + c1);
   }
-  if (n0 && p.splits[0] > 1) t += 0.03 * (double)n0 + 0.5;
-  if (n1 && p.splits[1] > 1) t += 0.015 * (double)n1 + 0.5;
+  if (n0 && p.splits[0] > 1) t += 0.06 * (double)n0 + 1.0;
+  if (n1 && p.splits[1] > 1) t += 0.03 * (double)n1 + 1.0;
   return t;
 }
 
@@ -104,7 +104,7 @@ Plan make_plan(int prefix_len, int q_len, int n_streams, int num_splits) {
     const int cus = cu_count();
     double best = 1e300;
     Plan trial = p;
-    for (int s0 = 1; s0 <= 16 && s0 <= p.n_tiles; ++s0) {
+    for (int s0 = 1; s0 <= 32 && s0 <= p.n_tiles; ++s0) {
       if (units0 == 0 && s0 > 1) break;
       set_splits(trial, 0, s0);
       if (trial.splits[0] != s0) continue;

@@ -12,9 +12,9 @@ constexpr int kDRope = 64;
 constexpr int kMaxQ = 64;
 
 // verify_attn tiling: one workgroup = 4 waves = 2 tree nodes x 64 heads; keys are staged into
-// LDS 64 rows at a time.
+// LDS 32 rows at a time.
 constexpr int kQueriesPerWG = 2;
-constexpr int kTileKeys = 64;
+constexpr int kTileKeys = 32;
 constexpr int kWGThreads = 256;
 
 // The launch holds two groups of workgroups.  Group 0: node pairs (2p, 2p + 1), p < q_len / 2.
@@ -38,7 +38,7 @@ struct VerifyArgs {
   int n_streams;
   int kv_rows;
   int n_pairs;         // q_len / 2
-  int n_tiles;         // ceil((prefix_len + q_len) / 64)
+  int n_tiles;         // ceil((prefix_len + q_len) / kTileKeys)
   int splits[2];
   int tiles_per_split[2];
   int wg_count0;       // workgroups of group 0; group 1 follows

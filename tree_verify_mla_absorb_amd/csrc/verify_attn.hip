@@ -12,20 +12,27 @@
 // staged into LDS once per workgroup and consumed by all 128 query-head rows of that workgroup
 // as bf16 MFMA contractions:
 //
-//   S^T[key, qh] = K[key, 0:576] . Q^T[0:576, qh]          (A = K from LDS, B = Q in VGPRs)
+//   S^T[key, qh] = K[key, 0:576] . Q^T[0:576, qh]          (A = K from LDS, B = Q)
 //   O^T[dim, qh] += V^T[dim, key] . P^T[key, qh]            (A = V^T via LDS transpose reads,
-//                                                            B = P^T straight from S^T's acc)
+//                                                            B = P^T, published through LDS)
 //
 // Computing S^T (keys as MFMA rows) puts one query-head column in each lane, so the softmax
-// statistics are per-lane values plus one cross-half swap, and the accumulator layout of S^T
-// is already the B-operand layout the PV product needs (the key order inside the 16-key
+// statistics are per-lane values plus one cross-half exchange, and the accumulator layout of
+// S^T is already the B-operand layout the PV product needs (the key order inside each 16-key
 // contraction is permuted identically on the V side).
 //
-// Workgroup = 4 waves over 2 tree nodes x 64 heads.  For the scores, wave w owns node
-// (2 * group + w / 2) and heads 32 * (w & 1) .. +31, so the tree mask is wave-uniform: one 64-bit
-// ancestor-or-self mask walked from parents[] with a walk bounded by q_len (the bounded-walk
-// lesson of "The Microsecond Verdict", section "The Crash That Demanded a Fix").  For the value
-// product the waves split the 512 latent dims instead and share the probabilities through LDS.
+// Workgroup = 4 waves over 2 tree nodes x 64 heads = 4 head blocks of 32 query-heads.  For the
+// scores, wave w owns head block w: node (first + w / 2), heads 32 (w & 1) .. +31, so the tree
+// mask is wave-uniform -- one 64-bit ancestor-or-self mask walked from parents[] with a walk
+// bounded by q_len (the bounded-walk lesson of "The Microsecond Verdict", section "The Crash
+// That Demanded a Fix").  For the value product the waves split the 512 latent dims instead
+// (wave w: dims 128 w .. +127 of all four head blocks) and share the probabilities through
+// LDS, so each V^T fragment read feeds four MFMAs.
+//
+// Pipeline, per 32-key tile t (one workgroup barrier per tile):
+//   wait for tile t's rows, barrier, start staging tile t + 1 (three LDS stages in a ring),
+//   scores of tile t, then the value product of tile t - 1 (whose probabilities were published
+//   before the barrier) next to the softmax of tile t, then publish tile t's probabilities.
 
 #include "kernels.h"
 
@@ -42,26 +49,31 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // LDS layout.
-//   latent stages 0/1: 64 rows x 1040 B (1024 B of c_kv + 16 B pad), double-buffered.  Key k of
-//       the tile lives in row rho(k), rho swapping the two 2-bit halves of k's low nibble.  With
-//       the pad, the 16 rows read by one ds_read_b128 phase land on 16 distinct bank quads and
-//       the 4 rows x 64 B read by 32 lanes of a ds_read_b64_tr_b16 land on 4 distinct 16-bank
-//       groups; every address is a per-lane base plus an immediate.
-//   rotary buffer: chunk-major, [16-byte chunk 8][key 64][16 B], so the 16 keys read by one
-//       ds_read_b128 phase are 256 contiguous bytes.  Single-buffered: it is only read by the
-//       score product, so the next tile's rows are loaded once every wave is past its scores.
-//   P buffer: bf16 probabilities of the tile, [head block 4][16-key slice 4][lane 64][16 B],
+//   stage s (ring of three), one 32-key tile each:
+//     latent: 32 rows x 1040 B (1024 B of c_kv + 16 B pad).  Key k lives in row rho(k), rho
+//         swapping the two 2-bit halves of k's low nibble.  With the pad, the 16 rows read by
+//         one ds_read_b128 phase land on 16 distinct bank quads and the 4 rows x 64 B read by
+//         32 lanes of a ds_read_b64_tr_b16 land on 4 distinct 16-bank groups; every address is
+//         a per-lane base plus an immediate.
+//     rotary: chunk-major, [16-byte chunk 8][key 32][16 B]: the 16 keys read by one
+//         ds_read_b128 phase are 256 contiguous bytes.
+//   P buffers (two): bf16 probabilities of a tile, [head block 4][16-key slice 2][lane 64][16 B],
 //       written by the wave that computed the scores and read by all four waves.
+//   rotary queries: [wave 4][k-step 4][lane 64][16 B], staged once.
 constexpr int kRowBytesGlobal = kDLat * 2;                // 1024 B per c_kv row in HBM
 constexpr int kRowStride = kRowBytesGlobal + 16;          // 1040 B per latent row in LDS
-constexpr int kLatBytes = kTileKeys * kRowStride;         // 66560 B
-constexpr int kRopeRowBytes = kDRope * 2;                 // 128 B
-constexpr int kRopeOff = 2 * kLatBytes;
-constexpr int kPOff = kRopeOff + kTileKeys * kRopeRowBytes;
-constexpr int kPBytes = 4 * 4 * 64 * 16;                  // 16 KiB
-constexpr int kSmemBytes = kPOff + kPBytes;               // 157696 B
+constexpr int kRopeRowBytes = kDRope * 2;                 // 128 B per k_pe row in HBM
+constexpr int kLatBytes = kTileKeys * kRowStride;         // 33280 B
+constexpr int kRopeBytes = kTileKeys * kRopeRowBytes;     // 4096 B
+constexpr int kStageBytes = kLatBytes + kRopeBytes;       // 37376 B
+constexpr int kStages = 3;
+constexpr int kPBytes = 4 * 2 * 64 * 16;                  // 8 KiB per buffer
+constexpr int kPOff = kStages * kStageBytes;
+constexpr int kQpeOff = kPOff + 2 * kPBytes;
+constexpr int kSmemBytes = kQpeOff + 4 * 4 * 64 * 16;     // 144896 B
 // Scores are exponentiated against a per-head reference max taken from the first 32 keys.
 // If the true max ends above ref + kRefHi or below ref - kRefLo (log2 units) the workgroup
 // repeats its key range once with the exact max as reference.  Inside the window every
@@ -72,14 +84,18 @@ constexpr float kRefLo = 32.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 // Buffer resource word 3 for gfx9-family raw (untyped, stride 0) buffers.
 constexpr int kBufferDword3 = 0x00020000;
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-// K fragments read ahead of the score MFMA that consumes them (LDS latency ~ 4 MFMAs).
+// s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: expcnt and lgkmcnt fields at their
+// maximum).  Issued through the builtin, the compiler's own wait tracking sees it and drops
+// any later wait it would otherwise place inside the key loop for its own loads.
+constexpr int kWaitVmcnt0 = 0x0F70;
+// Score operands read ahead of the MFMA that consumes them, in k-steps.
 constexpr int kKAhead = 4;
+// Score k-step at which the first reads of the following value product are issued.
+constexpr int kHookStep = 34;
+// Value step that reads the probabilities of the second 16-key slice.
+constexpr int kP1Step = 3;
+
+static_assert(kTileKeys == 32, "the layout above is written for 32-key tiles");
 
 __device__ __forceinline__ int rho(int k) { return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3); }
 
@@ -91,8 +107,9 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, unsigned bytes) {
 
 // One wave instruction of direct global->LDS staging: lane i's 16 bytes at
 // rsrc + soff + voff land at LDS byte lds_addr + 16 i.  Issued from asm so that the compiler
-// does not order later LDS reads of the *other* stage behind it; the consumer waits with an
-// explicit vmcnt(0) and a workgroup barrier before reading the stage this wrote.
+// neither orders later LDS reads of other stages behind it nor folds it into its own wait
+// counting; the consumer waits on vmcnt explicitly and crosses a workgroup barrier before
+// reading the stage this wrote.  The loop issues no other vector-memory instruction.
 __device__ __forceinline__ void dma16(unsigned lds_addr, i32x4 rsrc, int voff, int soff) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
@@ -112,11 +129,6 @@ struct Flag {
   static constexpr bool value = B;
 };
 
-// Workgroup = 4 waves, 2 tree nodes x 64 heads = 4 head blocks of 32 query-heads.
-//   scores:  wave w computes S^T for head block w (node 2 g + w / 2, heads 32 (w & 1) ..+31)
-//            over the tile's 64 keys, turns it into bf16 probabilities and publishes them;
-//   values:  wave w accumulates O^T for latent dims 128 w .. 128 w + 127 of all 4 head blocks,
-//            so each V^T fragment read from LDS feeds four MFMAs.
 __global__ void __attribute__((amdgpu_flat_work_group_size(kWGThreads, kWGThreads),
                                amdgpu_waves_per_eu(1, 1)))
 verify_attn_kernel(VerifyArgs a) {
@@ -178,54 +190,57 @@ verify_attn_kernel(VerifyArgs a) {
 
   // Q^T fragments of this wave's head block: lane holds head `head`, dims 16 ks + 8 g .. +7.
   // The 32 latent k-steps stay in VGPRs for the whole key range; the 4 rotary k-steps are
-  // re-read (L1/L2 hits) at the start of every tile, which keeps the register file within
-  // budget.
+  // staged once into LDS (the register file is full: O^T alone takes all 256 AGPRs).
   const size_t qrow = ((size_t)s * Q + qc) * kHeads + head;
   bf16x8 qf[32];
   {
     const uint16_t* ql = a.q_lat + qrow * kDLat + g * 8;
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(ql + ks * 16);
-  }
-  const uint16_t* const qp_lane = a.q_pe + qrow * kDRope + g * 8;
-  bf16x8 qr[4];
-  auto load_qr = [&]() __attribute__((always_inline)) {
+    // Consume every fragment here, so the wait for these loads happens once, before the key
+    // loop: otherwise the loop's MFMAs carry waits that also drain the tile prefetch.
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qr[ks] = *reinterpret_cast<const bf16x8*>(qp_lane + ks * 16);
-  };
+    for (int ks = 0; ks < 32; ++ks) asm volatile("" : "+v"(qf[ks]));
+    const uint16_t* qp = a.q_pe + qrow * kDRope + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      *reinterpret_cast<bf16x8*>(smem + kQpeOff + wave * 4096 + ks * 1024 + lane * 16) =
+          *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+  }
 
   // Staging of this stream's cache rows.  A latent row is one wave instruction (64 lanes x
-  // 16 B); rotary instruction c moves 16-byte chunk c of all 64 rows (lane = key).  Rows past
-  // the end of the cache are clamped to the last row: their scores are masked out.
+  // 16 B); the rotary instruction of wave w moves 16-byte chunks 2w, 2w + 1 of all 32 rows
+  // (lanes 0-31: chunk 2w, lanes 32-63: chunk 2w + 1, lane & 31 = key).  Rows past the end of
+  // the cache are clamped to the last row: their scores are masked out.
   const i32x4 ckv_rs = buffer_rsrc(a.ckv + (size_t)s * a.kv_rows * kDLat, (unsigned)a.kv_rows * kDLat * 2);
   const i32x4 kpe_rs = buffer_rsrc(a.kpe + (size_t)s * a.kv_rows * kDRope, (unsigned)a.kv_rows * kDRope * 2);
   const unsigned smem_base = (unsigned)(size_t)((__attribute__((address_space(3))) unsigned char*)smem);
   const int lane16 = lane << 4;
-  auto load_latent = [&](int t, int stg) __attribute__((always_inline)) {
+  const int rope_lane = (lane & 31) * kRopeRowBytes + (lane >> 5) * 16;  // key row + chunk parity
+  auto stage_tile = [&](int t, int stg) __attribute__((always_inline)) {
+    const unsigned base = smem_base + stg * kStageBytes;
     const int key0 = t * kTileKeys;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int row = wave * 16 + rr;
+    for (int rr = 0; rr < kTileKeys / 4; ++rr) {
+      const int row = wave * (kTileKeys / 4) + rr;
       const int key = min(key0 + rho(row), L - 1);  // rho is its own inverse
-      dma16(__builtin_amdgcn_readfirstlane(smem_base + stg * kLatBytes + row * kRowStride), ckv_rs, lane16,
+      dma16(__builtin_amdgcn_readfirstlane(base + row * kRowStride), ckv_rs, lane16,
             __builtin_amdgcn_readfirstlane(key * kRowBytesGlobal));
     }
-  };
-  auto load_rope = [&](int t) __attribute__((always_inline)) {
-    const int voff = min(t * (kTileKeys * kRopeRowBytes) + (lane16 << 3), (L - 1) * kRopeRowBytes);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = wave * 2 + i;
-      dma16(__builtin_amdgcn_readfirstlane(smem_base + kRopeOff + c * 1024), kpe_rs, voff,
-            __builtin_amdgcn_readfirstlane(c * 16));
-    }
+    // rotary: keys past the end are clamped per lane
+    const int over = key0 + (lane & 31) - (L - 1);
+    const int voff = rope_lane - (over > 0 ? over * kRopeRowBytes : 0);
+    dma16(__builtin_amdgcn_readfirstlane(base + kLatBytes + wave * 1024), kpe_rs, voff,
+          __builtin_amdgcn_readfirstlane(key0 * kRopeRowBytes + wave * 32));
   };
 
-  // Per-lane LDS byte offsets (sub-tile, k-step, slice and block parts are immediates).
-  //  K reads: key jt*32 + c32 -> row jt*32 + rho(c32); 16-byte chunk 2 ks + g.
+  // Per-lane LDS byte offsets (k-step, slice and block parts are immediates).
+  //  K reads: key c32 -> row rho(c32); 16-byte chunk 2 ks + g.
   const int k_off = rho(c32) * kRowStride + (g << 4);
-  //  rotary K reads: key jt*32 + c32, chunk 2 ks + g
-  const int r_off = kRopeOff + g * 1024 + c32 * 16;
+  //  rotary K reads: key c32, chunk 2 ks + g
+  const int r_off = kLatBytes + g * 512 + c32 * 16;
+  //  rotary Q reads
+  const unsigned char* const qpe_lds = smem + kQpeOff + wave * 4096 + lane16;
   //  V^T transpose reads.  A ds_read_b64_tr_b16 serves 16 lanes from 4 rows x 4 chunks of 4
   //  bf16: lane (4 r + q) of a 16-lane group points at key r, dims 4q..4q+3 of the group's 16
   //  dims, and output lane j receives dim j of those 4 keys.  For a 16-key slice the two reads
@@ -235,8 +250,6 @@ verify_attn_kernel(VerifyArgs a) {
   const int q4 = lane & 3;
   const int tr_off = (4 * r4 + g) * kRowStride + ((((lane >> 4) & 1) << 1 | (q4 >> 1)) << 4) + ((q4 & 1) << 3) +
                      wave * 256;  // this wave's 128 latent dims
-  unsigned char* const p_mine = smem + kPOff + wave * 4096 + lane16;
-  const unsigned char* const p_all = smem + kPOff + lane16;
 
   f32x16 o[4][4];        // [head block][32-dim block]: dims 128 wave + 32 db + 8 (i / 4) + 4 g + i % 4
   float m_ref = 0.f;     // reference max (log2 units) of this lane's head, equal in both halves
@@ -247,132 +260,157 @@ verify_attn_kernel(VerifyArgs a) {
   const int t_end = min(a.n_tiles, t_begin + a.tiles_per_split[grp]);
   const int t_mask = max(t_begin, min(t_end, P / kTileKeys));  // first tile holding tree keys
 
-  // One 64-key tile held in stage `stg`: scores, probabilities, publish, values.
-  auto tile = [&](int t, int stg, auto masked_tag, auto first_tag) __attribute__((always_inline)) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    constexpr bool kFirst = decltype(first_tag)::value;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t staged; every wave is done with tile t - 1
-    const unsigned char* lat = smem + stg * kLatBytes;
-    const bool prefetch = t + 1 < t_end;
-    load_qr();  // rotary query fragments: consumed after the first 32 latent k-steps
-
-    // ---- per 32-key half: scores S^T (32 keys x 32 heads, K over 576 dims), visibility,
-    //      probabilities against the reference max, published as bf16
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      f32x16 st = f32x16{};
-      const unsigned char* kp = lat + k_off + jt * 32 * kRowStride;
-#pragma unroll
-      for (int ks = 0; ks < 32; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kp + ks * 32);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st, 0, 0, 0);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(smem + r_off + ks * 2048 + jt * 512);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qr[ks], st, 0, 0, 0);
-      }
-      // Schedule: kKAhead K reads in flight ahead of the MFMA that consumes them.
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKAhead, 0);
-#pragma unroll
-      for (int i = 0; i < 36 - kKAhead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKAhead, 0);
-      if (jt == 0) {
-        // Prefetch the next tile's latent rows into the other stage (nobody reads it now).
-        // Issued only after the rotary fragments are consumed, so that the wait for those
-        // never waits for the staging as well.
-        __builtin_amdgcn_sched_barrier(0);
-        if (prefetch) load_latent(t + 1, stg ^ 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // accumulator entry i holds key 8 (i / 4) + 4 g + i % 4 of the half
-      if constexpr (kMasked) {
-        const int kb0 = t * kTileKeys + jt * 32 + 4 * g - P;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int rel = kb0 + 8 * (i >> 2) + (i & 3);
-          const unsigned sh = (unsigned)min(max(rel, 0), 63);
-          const bool vis = (rel < 0) | ((rel < Q) & (unsigned)((anc >> sh) & 1ull));
-          st[i] = vis ? st[i] : -INFINITY;
-        }
-      }
-      float mx = st[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, st[i]);
-      mx *= cs;
-      mx_run = fmaxf(mx_run, mx);
-      if constexpr (kFirst) {
-        if (jt == 0) {
-          const float m0 = half_max(mx);
-          m_ref = m0 == -INFINITY ? 0.f : m0;
-        }
-      }
-      float psum = 0.f;
-      bf16x8 pb[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(st[i], cs, -m_ref));
-        psum += pv;
-        pb[i >> 3][i & 7] = (__bf16)pv;
-      }
-      l_run += psum;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) *reinterpret_cast<bf16x8*>(p_mine + (jt * 2 + u) * 1024) = pb[u];
-    }
-    __syncthreads();  // all four head blocks' probabilities published; rotary rows consumed
-    if (prefetch) load_rope(t + 1);
-
-    // ---- O^T += V^T P^T: 4 slices of 16 keys, 4 dim blocks x 4 head blocks per slice.
-    //      Step k = (slice, dim block); the reads of step k + 1 are issued before the MFMAs of
-    //      step k so that LDS latency overlaps the matrix work.
-    auto vfrag = [&](int k) __attribute__((always_inline)) -> bf16x8 {
-      const int sl = k >> 2, db = k & 3;
-      const unsigned char* vp = lat + tr_off + ((sl >> 1) * 32 + (sl & 1) * 16) * kRowStride + db * 64;
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
-      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 2 * kRowStride));
-      return __builtin_bit_cast(bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+  // ---- S^T of a tile held in stage stg: 32 latent + 4 rotary k-steps
+  auto score_mma = [&](int stg, auto&& hook) __attribute__((always_inline)) -> f32x16 {
+    const unsigned char* st_base = smem + stg * kStageBytes;
+    auto kfrag = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
+      return ks < 32 ? *reinterpret_cast<const bf16x8*>(st_base + k_off + ks * 32)
+                     : *reinterpret_cast<const bf16x8*>(st_base + r_off + (ks - 32) * 1024);
     };
-    bf16x8 pf[4];
+    // K fragments are read kKAhead k-steps ahead of their MFMA (the rotary Q fragments, also in
+    // LDS, at their MFMA); a scheduling barrier after each k-step keeps that order (left alone,
+    // the scheduler moves each read next to its use, and every MFMA waits out a full LDS
+    // latency).  hook() issues the first reads of the value product that follows.
+    auto qpe_frag = [&](int r) __attribute__((always_inline)) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(qpe_lds + r * 1024);
+    };
+    bf16x8 kb[kKAhead];
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) pf[hb] = *reinterpret_cast<const bf16x8*>(p_all + hb * 4096);
-    bf16x8 vf = vfrag(0);
+    for (int j = 0; j < kKAhead; ++j) kb[j] = kfrag(j);
+    f32x16 st = f32x16{};
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int sl = k >> 2, db = k & 3;
-      const bf16x8 vcur = vf;
-      bf16x8 pcur[4];
+    for (int ks = 0; ks < 36; ++ks) {
+      const bf16x8 kcur = kb[ks % kKAhead];
+      const bf16x8 qcur = ks < 32 ? qf[ks] : qpe_frag(ks - 32);
+      if (ks + kKAhead < 36) kb[ks % kKAhead] = kfrag(ks + kKAhead);
+      if (ks == kHookStep) hook();
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qcur, st, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return st;
+  };
+
+  // ---- probabilities of accumulator entries 2 k, 2 k + 1 of tile t (entry i holds key
+  //      8 (i / 4) + 4 g + i % 4 of the tile): visibility, running raw max, exp2 against the
+  //      reference, running sum, bf16 packing.
+  auto prob_pair = [&](const f32x16& st, int t, int k, auto masked_tag, bf16x8 (&pb)[2], float& psum,
+                       float& mx) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb) pcur[hb] = pf[hb];
-      if (k + 1 < 16) {
-        vf = vfrag(k + 1);
-        if (((k + 1) & 3) == 0) {
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb)
-            pf[hb] = *reinterpret_cast<const bf16x8*>(p_all + hb * 4096 + ((k + 1) >> 2) * 1024);
-        }
+    for (int e = 2 * k; e < 2 * k + 2; ++e) {
+      float x = st[e];
+      if constexpr (kMasked) {
+        const int rel = t * kTileKeys + 4 * g - P + 8 * (e >> 2) + (e & 3);
+        const unsigned sh = (unsigned)min(max(rel, 0), 63);
+        const bool vis = (rel < 0) | ((rel < Q) & (unsigned)((anc >> sh) & 1ull));
+        x = vis ? x : -INFINITY;
       }
-      (void)sl;
+      mx = fmaxf(mx, x);
+      const float pv = __builtin_amdgcn_exp2f(fmaf(x, cs, -m_ref));
+      psum += pv;
+      pb[e >> 3][e & 7] = (__bf16)pv;
+    }
+  };
+  auto publish = [&](int pbuf, int u, const bf16x8& v) __attribute__((always_inline)) {
+    *reinterpret_cast<bf16x8*>(smem + kPOff + pbuf * kPBytes + wave * 2048 + lane16 + u * 1024) = v;
+  };
+
+  // ---- values of a tile held in stage stg with probabilities in pbuf: O^T += V^T P^T,
+  //      2 slices of 16 keys x 4 dim blocks = 8 steps of 4 MFMAs (one per head block).
+  //      value_prologue reads the first operands (P of slice 0, V^T of step 0); step k reads V^T
+  //      of step k + 1 (and, at k = kP1Step, P of slice 1), and side(k) -- VALU work of the next
+  //      tile -- shares step k with the MFMAs.  A scheduling barrier closes each step.
+  auto vfrag = [&](int stg, int k) __attribute__((always_inline)) -> bf16x8 {
+    const unsigned char* vp = smem + stg * kStageBytes + tr_off + (k >> 2) * 16 * kRowStride + (k & 3) * 64;
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 2 * kRowStride));
+    return __builtin_bit_cast(bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+  };
+  auto pfrag = [&](int pbuf, int hb, int slice) __attribute__((always_inline)) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(smem + kPOff + pbuf * kPBytes + hb * 2048 + slice * 1024 + lane16);
+  };
+  auto value_prologue = [&](int stg, int pbuf, bf16x8 (&p0)[4], bf16x8& vf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) p0[hb] = pfrag(pbuf, hb, 0);
+    vf = vfrag(stg, 0);
+  };
+  auto values = [&](int stg, int pbuf, bf16x8 (&p0)[4], bf16x8& vf, auto&& side) __attribute__((always_inline)) {
+    bf16x8 p1[4];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bf16x8 vcur = vf;
+      if (k + 1 < 8) vf = vfrag(stg, k + 1);
+      if (k == kP1Step) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) p1[hb] = pfrag(pbuf, hb, 1);
+      }
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
-        o[hb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, pcur[hb], o[hb][db], 0, 0, 0);
+        o[hb][k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, k < 4 ? p0[hb] : p1[hb], o[hb][k & 3], 0, 0, 0);
+      side(k);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // Schedule: the reads of step k + 1 (two V^T halves, plus the next slice's four P^T
-    // fragments at a slice boundary) are issued before the MFMAs of step k.
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 1);
+  };
+  auto no_side = [](int) __attribute__((always_inline)) {};
+  auto no_hook = []() __attribute__((always_inline)) {};
+
+  // ---- one pipeline step: tile t's rows are in stage (t - t_begin) % 3 (staged one step
+  //      earlier); the previous tile's probabilities are in P buffer (t - t_begin + 1) & 1.
+  //      A steady step runs the value product of tile t - 1 with the softmax of tile t spread
+  //      between its MFMAs.  The first step of a pass has no previous tile; on the first pass it
+  //      also sets the reference max from this tile before any exponential.
+  auto step = [&](int t, auto masked_tag, auto first_tag, auto set_ref_tag) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first_tag)::value;
+    constexpr bool kSetRef = decltype(set_ref_tag)::value;
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    const int i = t - t_begin;
+    const int stg = i % kStages;
+    const int pbuf = i & 1;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();  // tile t staged and published tile t - 1 visible; tile t - 2 released
+    if (t + 1 < t_end) stage_tile(t + 1, (i + 1) % kStages);
+    bf16x8 p0[4], vf;
+    const int prev_stg = (i + 2) % kStages, prev_pbuf = (i + 1) & 1;
+    f32x16 st;
+    if constexpr (kFirst)
+      st = score_mma(stg, no_hook);
+    else
+      st = score_mma(stg, [&]() __attribute__((always_inline)) { value_prologue(prev_stg, prev_pbuf, p0, vf); });
+    bf16x8 pb[2];
+    float psum = 0.f, mx = -INFINITY;
+    if constexpr (kFirst) {
+      if constexpr (kSetRef) {
+        float m = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      if (k < 15) {
-        if (((k + 1) & 3) == 0)
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 1);
-        else
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+        for (int e = 0; e < 16; ++e) {
+          float x = st[e];
+          if constexpr (kMasked) {
+            const int rel = t * kTileKeys + 4 * g - P + 8 * (e >> 2) + (e & 3);
+            const unsigned sh = (unsigned)min(max(rel, 0), 63);
+            const bool vis = (rel < 0) | ((rel < Q) & (unsigned)((anc >> sh) & 1ull));
+            x = vis ? x : -INFINITY;
+          }
+          m = fmaxf(m, x);
+        }
+        const float m0 = half_max(m * cs);
+        m_ref = m0 == -INFINITY ? 0.f : m0;
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) prob_pair(st, t, k, masked_tag, pb, psum, mx);
+      publish(pbuf, 0, pb[0]);
+      publish(pbuf, 1, pb[1]);
+    } else {
+      // Move the scores out of the accumulator registers before the value product, which
+      // needs every one of them for O^T.
+#pragma unroll
+      for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(st[e]));
+      values(prev_stg, prev_pbuf, p0, vf, [&](int k) __attribute__((always_inline)) {
+        prob_pair(st, t, k, masked_tag, pb, psum, mx);
+        if ((k & 3) == 3) publish(pbuf, k >> 2, pb[k >> 2]);
+      });
     }
+    l_run += psum;
+    mx_run = fmaxf(mx_run, mx * cs);
   };
 
   for (int attempt = 0; attempt < 2; ++attempt) {
@@ -383,18 +421,31 @@ verify_attn_kernel(VerifyArgs a) {
     l_run = 0.f;
     mx_run = -INFINITY;
 
-    load_latent(t_begin, 0);
-    load_rope(t_begin);
+    stage_tile(t_begin, 0);
     int t = t_begin;
-    if (attempt == 0) {  // the first 32 keys of the range set the reference max
+    // first tile: sets the reference max on the first pass, no value product yet
+    if (attempt == 0) {
       if (t < t_mask)
-        tile(t, 0, Flag<false>{}, Flag<true>{});
+        step(t, Flag<false>{}, Flag<true>{}, Flag<true>{});
       else
-        tile(t, 0, Flag<true>{}, Flag<true>{});
-      ++t;
+        step(t, Flag<true>{}, Flag<true>{}, Flag<true>{});
+    } else {  // the second pass keeps the exact max found by the first
+      if (t < t_mask)
+        step(t, Flag<false>{}, Flag<true>{}, Flag<false>{});
+      else
+        step(t, Flag<true>{}, Flag<true>{}, Flag<false>{});
     }
-    for (; t < t_mask; ++t) tile(t, (t - t_begin) & 1, Flag<false>{}, Flag<false>{});
-    for (; t < t_end; ++t) tile(t, (t - t_begin) & 1, Flag<true>{}, Flag<false>{});
+    ++t;
+    for (; t < t_mask; ++t) step(t, Flag<false>{}, Flag<false>{}, Flag<false>{});
+    for (; t < t_end; ++t) step(t, Flag<true>{}, Flag<false>{}, Flag<false>{});
+    // last tile's values
+    __syncthreads();
+    {
+      const int last_stg = (t_end - 1 - t_begin) % kStages, last_pbuf = (t_end - 1 - t_begin) & 1;
+      bf16x8 p0[4], vf;
+      value_prologue(last_stg, last_pbuf, p0, vf);
+      values(last_stg, last_pbuf, p0, vf, no_side);
+    }
 
     // Was the reference max a safe choice for every head of the workgroup?
     const float mfull = half_max(mx_run);
@@ -408,9 +459,8 @@ verify_attn_kernel(VerifyArgs a) {
   }
 
   // ---- finalize: denominators of all four head blocks through LDS
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no staging may still be in flight
   const float lt = half_sum(l_run);
-  float* l_sh = reinterpret_cast<float*>(smem + kPOff);  // the P buffer is free after the last barrier
+  float* l_sh = reinterpret_cast<float*>(smem + kPOff);  // the P buffers are free after the last barrier
   if (g == 0) l_sh[wave * 32 + c32] = lt;
   const int part_rows = grp == 0 ? a.n_streams * a.n_pairs * 2 * kHeads : a.n_streams * kHeads;
   if (active && g == 0) {
