@@ -90,6 +90,12 @@ constexpr int kBufferDword3 = 0x00020000;
 constexpr int kWaitVmcnt0 = 0x0F70;
 // Score operands read ahead of the MFMA that consumes them, in k-steps.
 constexpr int kKAhead = 4;
+// Staging instructions per wave and tile: 8 latent rows and one rotary instruction.
+constexpr int kStageInstrs = kTileKeys / 4 + 1;
+// Staging instructions of the next tile issued inside the score chain (one every kDmaEvery
+// k-steps); the rest go into the first value steps.
+constexpr int kDmaEvery = 5;
+constexpr int kDmaInScores = 7;
 // Score k-step at which the first reads of the following value product are issued.
 constexpr int kHookStep = 34;
 // Value step that reads the probabilities of the second 16-key slice.
@@ -118,6 +124,23 @@ __device__ __forceinline__ void dma16(unsigned lds_addr, i32x4 rsrc, int voff, i
       :
       : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
       : "memory");
+}
+
+// One k-step of the score chain, S^T += K Q^T, with the accumulator in VGPRs.  Issued from
+// asm because the compiler gives every MFMA of this kernel an AGPR accumulator, and an AGPR
+// score tile would evict a block of O^T (which fills all 256 AGPRs) on every key tile.  The
+// chain accumulates in place (the source C operand is the destination itself, which the
+// matrix core forwards back to back); the first step starts from 0.  The last step ends with
+// 18 wait states so that the VALU reads of the scores that follow see the final result
+// (an 8-pass XDL result needs 12 before a VALU read on gfx950).
+__device__ __forceinline__ void score_step(f32x16& st, const bf16x8& k, const bf16x8& q, int u) {
+  if (u == 0)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(st) : "v"(k), "v"(q));
+  else if (u == 35)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 1"
+                 : "+v"(st) : "v"(k), "v"(q));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(st) : "v"(k), "v"(q));
 }
 
 // Combine the two lane halves that hold the same head (lanes l and l ^ 32).
@@ -214,24 +237,32 @@ verify_attn_kernel(VerifyArgs a) {
   // the cache are clamped to the last row: their scores are masked out.
   const i32x4 ckv_rs = buffer_rsrc(a.ckv + (size_t)s * a.kv_rows * kDLat, (unsigned)a.kv_rows * kDLat * 2);
   const i32x4 kpe_rs = buffer_rsrc(a.kpe + (size_t)s * a.kv_rows * kDRope, (unsigned)a.kv_rows * kDRope * 2);
+  const i32x4 ckv_none = buffer_rsrc(a.ckv, 0u), kpe_none = buffer_rsrc(a.kpe, 0u);
   const unsigned smem_base = (unsigned)(size_t)((__attribute__((address_space(3))) unsigned char*)smem);
   const int lane16 = lane << 4;
   const int rope_lane = (lane & 31) * kRopeRowBytes + (lane >> 5) * 16;  // key row + chunk parity
-  auto stage_tile = [&](int t, int stg) __attribute__((always_inline)) {
+  // Wave instruction j of staging tile t into stage stg: j < 8 moves latent row 8 wave + j,
+  // j = 8 the wave's rotary chunks.  With empty resources (0 bytes) every lane is out of
+  // range: the instruction reads no memory, which lets the key loop issue it unconditionally.
+  auto stage_part = [&](int t, int stg, int j, const i32x4& crs, const i32x4& krs) __attribute__((always_inline)) {
     const unsigned base = smem_base + stg * kStageBytes;
     const int key0 = t * kTileKeys;
-#pragma unroll
-    for (int rr = 0; rr < kTileKeys / 4; ++rr) {
-      const int row = wave * (kTileKeys / 4) + rr;
+    if (j < kTileKeys / 4) {
+      const int row = wave * (kTileKeys / 4) + j;
       const int key = min(key0 + rho(row), L - 1);  // rho is its own inverse
-      dma16(__builtin_amdgcn_readfirstlane(base + row * kRowStride), ckv_rs, lane16,
+      dma16(__builtin_amdgcn_readfirstlane(base + row * kRowStride), crs, lane16,
             __builtin_amdgcn_readfirstlane(key * kRowBytesGlobal));
+    } else {
+      // rotary: keys past the end are clamped per lane
+      const int over = key0 + (lane & 31) - (L - 1);
+      const int voff = rope_lane - (over > 0 ? over * kRopeRowBytes : 0);
+      dma16(__builtin_amdgcn_readfirstlane(base + kLatBytes + wave * 1024), krs, voff,
+            __builtin_amdgcn_readfirstlane(key0 * kRopeRowBytes + wave * 32));
     }
-    // rotary: keys past the end are clamped per lane
-    const int over = key0 + (lane & 31) - (L - 1);
-    const int voff = rope_lane - (over > 0 ? over * kRopeRowBytes : 0);
-    dma16(__builtin_amdgcn_readfirstlane(base + kLatBytes + wave * 1024), kpe_rs, voff,
-          __builtin_amdgcn_readfirstlane(key0 * kRopeRowBytes + wave * 32));
+  };
+  auto stage_tile = [&](int t, int stg) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kStageInstrs; ++j) stage_part(t, stg, j, ckv_rs, kpe_rs);
   };
 
   // Per-lane LDS byte offsets (k-step, slice and block parts are immediates).
@@ -261,30 +292,40 @@ verify_attn_kernel(VerifyArgs a) {
   const int t_mask = max(t_begin, min(t_end, P / kTileKeys));  // first tile holding tree keys
 
   // ---- S^T of a tile held in stage stg: 32 latent + 4 rotary k-steps
-  auto score_mma = [&](int stg, auto&& hook) __attribute__((always_inline)) -> f32x16 {
+  auto score_mma = [&](int stg, auto&& hook, auto&& dma) __attribute__((always_inline)) -> f32x16 {
     const unsigned char* st_base = smem + stg * kStageBytes;
-    auto kfrag = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
-      return ks < 32 ? *reinterpret_cast<const bf16x8*>(st_base + k_off + ks * 32)
-                     : *reinterpret_cast<const bf16x8*>(st_base + r_off + (ks - 32) * 1024);
+    // k-step u: the 4 rotary k-steps first (both operands in LDS), then the 32 latent ones
+    // (Q in registers).
+    auto kfrag = [&](int u) __attribute__((always_inline)) -> bf16x8 {
+      return u < 4 ? *reinterpret_cast<const bf16x8*>(st_base + r_off + u * 1024)
+                   : *reinterpret_cast<const bf16x8*>(st_base + k_off + (u - 4) * 32);
     };
-    // K fragments are read kKAhead k-steps ahead of their MFMA (the rotary Q fragments, also in
-    // LDS, at their MFMA); a scheduling barrier after each k-step keeps that order (left alone,
-    // the scheduler moves each read next to its use, and every MFMA waits out a full LDS
-    // latency).  hook() issues the first reads of the value product that follows.
-    auto qpe_frag = [&](int r) __attribute__((always_inline)) -> bf16x8 {
-      return *reinterpret_cast<const bf16x8*>(qpe_lds + r * 1024);
+    auto qpe_frag = [&](int u) __attribute__((always_inline)) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(qpe_lds + u * 1024);
     };
-    bf16x8 kb[kKAhead];
+    // Operands are read kKAhead k-steps ahead of their MFMA; a scheduling barrier after each
+    // k-step keeps that order (left alone, the scheduler moves each read next to its use and
+    // every MFMA waits out a full LDS latency).  dma(j) issues staging instruction j of the
+    // next tile every kDmaEvery k-steps: a wave that issues them back to back stalls for most
+    // of their transfer, one spread between MFMAs costs little.  hook() issues the first reads
+    // of the value product.
+    bf16x8 kb[kKAhead], qb[4];
 #pragma unroll
-    for (int j = 0; j < kKAhead; ++j) kb[j] = kfrag(j);
-    f32x16 st = f32x16{};
+    for (int u = 0; u < kKAhead; ++u) {
+      kb[u] = kfrag(u);
+      if (u < 4) qb[u] = qpe_frag(u);
+    }
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) {
-      const bf16x8 kcur = kb[ks % kKAhead];
-      const bf16x8 qcur = ks < 32 ? qf[ks] : qpe_frag(ks - 32);
-      if (ks + kKAhead < 36) kb[ks % kKAhead] = kfrag(ks + kKAhead);
-      if (ks == kHookStep) hook();
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qcur, st, 0, 0, 0);
+    for (int u = kKAhead; u < 4; ++u) qb[u] = qpe_frag(u);
+    f32x16 st;
+#pragma unroll
+    for (int u = 0; u < 36; ++u) {
+      const bf16x8 kcur = kb[u % kKAhead];
+      const bf16x8 qcur = u < 4 ? qb[u] : qf[u - 4];
+      if (u + kKAhead < 36) kb[u % kKAhead] = kfrag(u + kKAhead);
+      if (u % kDmaEvery == 1 && u / kDmaEvery < kDmaInScores) dma(u / kDmaEvery);
+      if (u == kHookStep) hook();
+      score_step(st, kcur, qcur, u);
       __builtin_amdgcn_sched_barrier(0);
     }
     return st;
@@ -368,14 +409,19 @@ verify_attn_kernel(VerifyArgs a) {
     const int pbuf = i & 1;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();  // tile t staged and published tile t - 1 visible; tile t - 2 released
-    if (t + 1 < t_end) stage_tile(t + 1, (i + 1) % kStages);
+    const bool stage_next = t + 1 < t_end;
+    const i32x4 crs = stage_next ? ckv_rs : ckv_none, krs = stage_next ? kpe_rs : kpe_none;
+    auto dma = [&](int j) __attribute__((always_inline)) { stage_part(t + 1, (i + 1) % kStages, j, crs, krs); };
     bf16x8 p0[4], vf;
     const int prev_stg = (i + 2) % kStages, prev_pbuf = (i + 1) & 1;
     f32x16 st;
-    if constexpr (kFirst)
-      st = score_mma(stg, no_hook);
+    if constexpr (kFirst) {
+#pragma unroll
+      for (int j = kDmaInScores; j < kStageInstrs; ++j) dma(j);  // no value steps to carry them
+      st = score_mma(stg, no_hook, dma);
+    }
     else
-      st = score_mma(stg, [&]() __attribute__((always_inline)) { value_prologue(prev_stg, prev_pbuf, p0, vf); });
+      st = score_mma(stg, [&]() __attribute__((always_inline)) { value_prologue(prev_stg, prev_pbuf, p0, vf); }, dma);
     bf16x8 pb[2];
     float psum = 0.f, mx = -INFINITY;
     if constexpr (kFirst) {
@@ -400,11 +446,8 @@ verify_attn_kernel(VerifyArgs a) {
       publish(pbuf, 0, pb[0]);
       publish(pbuf, 1, pb[1]);
     } else {
-      // Move the scores out of the accumulator registers before the value product, which
-      // needs every one of them for O^T.
-#pragma unroll
-      for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(st[e]));
       values(prev_stg, prev_pbuf, p0, vf, [&](int k) __attribute__((always_inline)) {
+        if (k < kStageInstrs - kDmaInScores) dma(kDmaInScores + k);
         prob_pair(st, t, k, masked_tag, pb, psum, mx);
         if ((k & 3) == 3) publish(pbuf, k >> 2, pb[k >> 2]);
       });
