@@ -8,10 +8,12 @@ Everything is written out from its definition, in float64, with no blocking or f
 
 * ``verify_attn``   -- masked softmax attention in the absorbed MLA form.
 * ``compact_kv``    -- the out-of-place gather of the kept tree rows into the prefix.
+* ``tree_accept``   -- the greedy walk that picks the accepted path (the rows to keep).
 
 Every function is pinned by the CPU tests (brute force over all small trees, causal attention
 for a chain, per-path causal attention, closed forms, lse merge, equivariances, the absorb
-identity, and the race example).
+identity, the race example, and for acceptance: a chain closed form, the deepest-consistent-node
+formulation, and token-for-token agreement with autoregressive greedy decoding).
 """
 from .verify import (  # noqa: F401
     DEFAULT_SCALE,
@@ -25,3 +27,4 @@ from .verify import (  # noqa: F401
     visibility,
 )
 from .compact import compact_kv, validate_keep  # noqa: F401
+from .accept import tree_accept, tree_accept_streams, validate_parents  # noqa: F401

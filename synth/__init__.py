@@ -2,8 +2,10 @@
 
 This module holds none of the method's arithmetic.  It only draws inputs: bf16 activations
 (standard normal, rounded to bf16 by round-to-nearest-even on the fp32 bits), draft trees as
-``parents[]`` arrays, and an accepted root-to-leaf path per stream.  Both the fp64 oracle and the
-HIP path consume exactly these arrays, bit for bit.
+``parents[]`` arrays, an accepted root-to-leaf path per stream, and token ids for the tree
+nodes: the drafter's token of every node (distinct among siblings) and the target model's
+greedy token at every node, planted so that the accepted path is the drawn one.  Both the
+oracle and the HIP path consume exactly these arrays, bit for bit.
 
 Shapes follow the pages' engine ("Race Conditions, Buffer Aliasing, and the Architecture of a
 Native DDTree Inference Engine", section "The Cache Compaction Problem"): one latent cache per
@@ -27,6 +29,8 @@ D_ROPE = 64
 MAX_DEPTH = 15
 
 TAG_Q_LAT, TAG_Q_PE, TAG_CKV, TAG_KPE, TAG_PARENTS, TAG_LEAF = 0, 1, 2, 3, 4, 5
+TAG_DRAFT_TOK, TAG_TARGET_TOK, TAG_ACCEPT_DEPTH = 6, 7, 8
+VOCAB = 163840  # synthetic vocabulary size for token ids
 
 
 @dataclass(frozen=True)
@@ -114,6 +118,36 @@ def accepted_path(rng: np.random.Generator, parents: np.ndarray) -> np.ndarray:
     return np.array(path[::-1], dtype=np.int32)
 
 
+def draft_tokens(rng: np.random.Generator, parents: np.ndarray, vocab: int = VOCAB) -> np.ndarray:
+    """The drafter's token of every node: uniform ids, redrawn until distinct among siblings
+    (a drafter proposes distinct candidates at one position).  The root's entry is the last
+    committed token."""
+    q = len(parents)
+    tok = rng.integers(0, vocab, size=q, dtype=np.int64).astype(np.int32)
+    for j in range(1, q):
+        sib = [int(tok[k]) for k in range(1, j) if parents[k] == parents[j]]
+        while int(tok[j]) in sib:
+            tok[j] = rng.integers(0, vocab)
+    return tok
+
+
+def target_tokens(rng: np.random.Generator, parents: np.ndarray, draft: np.ndarray, path: np.ndarray,
+                  vocab: int = VOCAB) -> np.ndarray:
+    """The target model's greedy token at every node, planted so that greedy acceptance follows
+    ``path`` (a root-based chain of nodes) and stops at its last node: along the path the target
+    agrees with the next node's draft token, at the last node it differs from every child's
+    draft token, and elsewhere it is uniform."""
+    q = len(parents)
+    tgt = rng.integers(0, vocab, size=q, dtype=np.int64).astype(np.int32)
+    for k in range(len(path) - 1):
+        tgt[path[k]] = draft[path[k + 1]]
+    last = int(path[-1])
+    kids = {int(draft[j]) for j in range(q) if parents[j] == last}
+    while int(tgt[last]) in kids:
+        tgt[last] = rng.integers(0, vocab)
+    return tgt
+
+
 @dataclass
 class Batch:
     """Inputs for one launch, bf16 payloads stored as uint16 bit patterns."""
@@ -126,6 +160,8 @@ class Batch:
     parents: np.ndarray  # int32 [S, Q]
     keep: np.ndarray    # int32 [S, Q]  (accepted path, padded with -1)
     n_keep: np.ndarray  # int32 [S]
+    draft_tok: np.ndarray | None = None   # int32 [S, Q]
+    target_tok: np.ndarray | None = None  # int32 [S, Q]  (greedy acceptance yields keep)
     extra: dict = field(default_factory=dict)
 
 
@@ -140,6 +176,8 @@ def make_batch(w: Workload, streams: int | None = None, with_path: bool = True) 
     parents = np.empty((s_count, q), np.int32)
     keep = np.full((s_count, q), -1, np.int32)
     n_keep = np.zeros(s_count, np.int32)
+    draft = np.zeros((s_count, q), np.int32) if with_path else None
+    target = np.zeros((s_count, q), np.int32) if with_path else None
     for s in range(s_count):
         q_lat[s] = bf16_normal(rng_for(w.seed, s, TAG_Q_LAT), (q, h, D_LATENT))
         q_pe[s] = bf16_normal(rng_for(w.seed, s, TAG_Q_PE), (q, h, D_ROPE))
@@ -150,7 +188,21 @@ def make_batch(w: Workload, streams: int | None = None, with_path: bool = True) 
             path = accepted_path(rng_for(w.seed, s, TAG_LEAF), parents[s])
             keep[s, : len(path)] = path
             n_keep[s] = len(path)
-    return Batch(w, q_lat, q_pe, ckv, kpe, parents, keep, n_keep)
+            draft[s] = draft_tokens(rng_for(w.seed, s, TAG_DRAFT_TOK), parents[s])
+            target[s] = target_tokens(rng_for(w.seed, s, TAG_TARGET_TOK), parents[s], draft[s], path)
+    return Batch(w, q_lat, q_pe, ckv, kpe, parents, keep, n_keep, draft, target)
+
+
+def accept_case(seed: int, stream: int, q_len: int, tree: str = "uniform", vocab: int = VOCAB):
+    """A tree with tokens whose greedy acceptance stops at a uniformly drawn depth of a uniformly
+    drawn root-to-leaf path.  Returns (parents, draft, target, planted path)."""
+    parents = sample_parents(rng_for(seed, stream, TAG_PARENTS), q_len, tree)
+    full = accepted_path(rng_for(seed, stream, TAG_LEAF), parents)
+    depth = int(rng_for(seed, stream, TAG_ACCEPT_DEPTH).integers(0, len(full)))
+    path = full[: depth + 1]
+    draft = draft_tokens(rng_for(seed, stream, TAG_DRAFT_TOK), parents, vocab)
+    target = target_tokens(rng_for(seed, stream, TAG_TARGET_TOK), parents, draft, path, vocab)
+    return parents, draft, target, path
 
 
 def random_inputs(seed: int, streams: int, prefix: int, q_len: int, heads: int = HEADS,
