@@ -7,7 +7,14 @@
  *   ddtree_verify_attn   the tree-verify attention in MLA-absorb form with visibility masking
  *                        (section "The Mission: A Native DDTree Engine");
  *   ddtree_compact_kv    the post-accept gather of the kept tree rows into the prefix, free of
- *                        the in-place aliasing race (section "The Cache Compaction Problem").
+ *                        the in-place aliasing race (section "The Cache Compaction Problem");
+ *
+ * and the step between them, described on "The Microsecond Verdict: Validating a DDTree
+ * Kernel Fix Under Time Pressure":
+ *
+ *   ddtree_tree_accept   greedy acceptance of the verified tree (sections "The Crash That
+ *                        Demanded a Fix" and "What Was Learned");
+ *   ddtree_accept_compact  acceptance and compaction in one launch.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -147,6 +154,52 @@ typedef struct ddtree_kv_cache {
 int ddtree_compact_kv(const ddtree_kv_cache* cache, int prefix_len, const int32_t* keep,
                       const int32_t* n_keep, int keep_stride, int32_t* dev_status,
                       hipStream_t stream);
+
+/*
+ * ddtree_tree_accept -- greedy acceptance of the verified draft trees, one launch for all
+ * streams.
+ *
+ * For every stream s the walk starts at the root (node 0, always accepted).  From the current
+ * node c it moves to the lowest-index child j (parents[s][j] == c) with
+ * draft_tokens[s][j] == target_tokens[s][c], and stops when no child matches.  The walk visits
+ * strictly increasing nodes, so it ends within q_len nodes for any input (the bound that page
+ * adds against cyclic links).
+ *
+ * Arguments (device pointers, 4-byte aligned, densely packed):
+ *   parents        int32 [n_streams][q_len]   the tree, as for ddtree_verify_attn
+ *   draft_tokens   int32 [n_streams][q_len]   the drafter's token of each node (the root's
+ *                                             entry is not read)
+ *   target_tokens  int32 [n_streams][q_len]   the target model's greedy token after each node
+ *   keep           int32 [n_streams][keep_stride], keep_stride >= q_len: entries [0, n_keep[s])
+ *                  receive the accepted nodes (keep[s][0] = 0, strictly increasing); later
+ *                  entries are left unchanged.  This is the keep array of ddtree_compact_kv.
+ *   n_keep         int32 [n_streams]          the number of accepted nodes, 1..q_len
+ *   next_token     int32 [n_streams] or NULL  target_tokens[s][last accepted node]: the target's
+ *                                             token for the position after the accepted run
+ *   dev_status     optional device int32 status word, may be NULL
+ * A stream whose parents[] is not a valid tree (parents[0] == -1 and 0 <= parents[i] < i) gets
+ * n_keep = 0 and next_token = -1 and sets DDTREE_STATUS_BAD_PARENTS.
+ * Sizes: 1 <= q_len <= 64, 1 <= n_streams, keep_stride >= q_len.
+ * Errors: DDTREE_ERR_NULL / _SHAPE / _ALIGN / _ALIAS (an output overlapping an input or another
+ * output) / _HIP.
+ */
+int ddtree_tree_accept(const int32_t* parents, const int32_t* draft_tokens, const int32_t* target_tokens,
+                       int q_len, int n_streams, int32_t* keep, int keep_stride, int32_t* n_keep,
+                       int32_t* next_token, int32_t* dev_status, hipStream_t stream);
+
+/*
+ * ddtree_accept_compact -- ddtree_tree_accept and then ddtree_compact_kv on its keep / n_keep,
+ * in one launch (no host round trip, no second kernel).  Same arguments and results as the two
+ * calls in sequence, with the tree block of every stream at rows [prefix_len, prefix_len + q_len)
+ * of the cache: prefix_len + q_len <= cache->kv_rows and cache->n_streams == n_streams.
+ * A stream with a malformed tree keeps its cache rows bit-identical.
+ * Errors: as ddtree_tree_accept, plus the cache checks of ddtree_compact_kv (keep / n_keep /
+ * next_token must not overlap the cache either).
+ */
+int ddtree_accept_compact(const ddtree_kv_cache* cache, int prefix_len, const int32_t* parents,
+                          const int32_t* draft_tokens, const int32_t* target_tokens, int q_len,
+                          int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
+                          int32_t* dev_status, hipStream_t stream);
 
 /* Static text for a return code. */
 const char* ddtree_status_string(int code);

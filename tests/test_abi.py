@@ -130,3 +130,36 @@ def test_compact_argument_errors():
     assert compact(ckv=A + 8) == _lib.ERR_ALIGN
     assert compact(keep=E + 2) == _lib.ERR_ALIGN
     assert compact(kpe=A + 1024) == _lib.ERR_ALIAS
+
+
+def accept(parents=A, draft=B, target=C, q=9, s=2, keep=D, stride=9, n_keep=E, nxt=F, status=None):
+    return _lib.LIB.ddtree_tree_accept(parents, draft, target, q, s, keep, stride, n_keep, nxt, status, None)
+
+
+def test_accept_argument_errors():
+    for field in ("parents", "draft", "target", "keep", "n_keep"):
+        assert accept(**{field: None}) == _lib.ERR_NULL
+    assert accept(q=0) == _lib.ERR_SHAPE
+    assert accept(q=65, stride=65) == _lib.ERR_SHAPE
+    assert accept(s=0) == _lib.ERR_SHAPE
+    assert accept(stride=8) == _lib.ERR_SHAPE          # keep rows must hold a full-length path
+    assert accept(keep=D + 2) == _lib.ERR_ALIGN
+    assert accept(nxt=F + 1) == _lib.ERR_ALIGN
+    assert accept(keep=A) == _lib.ERR_ALIAS             # keep over parents
+    assert accept(n_keep=D + 8) == _lib.ERR_ALIAS       # n_keep inside keep
+    assert accept(nxt=E + 4) == _lib.ERR_ALIAS          # next_token over n_keep
+    assert accept(nxt=None, n_keep=C + 16) == _lib.ERR_ALIAS  # n_keep inside target
+
+
+def accept_compact(rows=300, s=2, prefix=100, q=9, keep=D, nxt=F, parents=A, cache=True):
+    c = _lib.KVCache(G, G + 0x10000000, rows, s)
+    return _lib.LIB.ddtree_accept_compact(ctypes.byref(c) if cache else None, prefix, parents, B, C, q, keep, q, E,
+                                          nxt, None, None)
+
+
+def test_accept_compact_argument_errors():
+    assert accept_compact(cache=False) == _lib.ERR_NULL
+    assert accept_compact(parents=None) == _lib.ERR_NULL
+    assert accept_compact(prefix=292) == _lib.ERR_SHAPE   # tree block past the cache rows
+    assert accept_compact(s=0) == _lib.ERR_SHAPE
+    assert accept_compact(keep=G + 64) == _lib.ERR_ALIAS  # keep inside the latent cache

@@ -1,14 +1,17 @@
-"""MI355X (gfx950) tree-verify MLA-absorb attention and race-free KV compaction.
+"""MI355X (gfx950) tree-verify MLA-absorb attention, greedy tree acceptance and race-free KV
+compaction.
 
 The compute lives in ``libddtree.so`` (C ABI, ``include/ddtree.h``); this package only binds it::
 
-    from tree_verify_mla_absorb_amd import verify_attn, verify_attn_ex, compact_kv
+    from tree_verify_mla_absorb_amd import verify_attn, verify_attn_ex, tree_accept, accept_compact, compact_kv
 """
 from ._lib import (  # noqa: F401
     DDTreeError,
+    accept_compact,
     compact_kv,
     num_splits,
     status_string,
+    tree_accept,
     verify_attn,
     verify_attn_ex,
     version,

@@ -36,6 +36,10 @@ def _load() -> ctypes.CDLL:
     lib.ddtree_verify_attn_num_splits.restype = i32
     lib.ddtree_compact_kv.argtypes = [vp, i32, vp, vp, i32, vp, vp]
     lib.ddtree_compact_kv.restype = i32
+    lib.ddtree_tree_accept.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp]
+    lib.ddtree_tree_accept.restype = i32
+    lib.ddtree_accept_compact.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp]
+    lib.ddtree_accept_compact.restype = i32
     lib.ddtree_status_string.argtypes = [i32]
     lib.ddtree_status_string.restype = ctypes.c_char_p
     lib.ddtree_version.argtypes = []
@@ -51,6 +55,8 @@ EXPORTED = (
     "ddtree_verify_attn_workspace_size",
     "ddtree_verify_attn_num_splits",
     "ddtree_compact_kv",
+    "ddtree_tree_accept",
+    "ddtree_accept_compact",
     "ddtree_status_string",
     "ddtree_version",
 )
@@ -181,3 +187,55 @@ def compact_kv(ckv, kpe, prefix_len: int, keep, n_keep, *, status=None, stream=N
     cache = KVCache(ckv.data_ptr(), kpe.data_ptr(), int(rows), int(s))
     _check(LIB.ddtree_compact_kv(ctypes.byref(cache), int(prefix_len), _ptr(keep), _ptr(n_keep), int(keep.shape[1]),
                                  _ptr(status), _stream(stream)))
+
+
+def _accept_inputs(parents, draft_tokens, target_tokens, keep, n_keep, next_token, status):
+    for t, name in ((parents, "parents"), (draft_tokens, "draft_tokens"), (target_tokens, "target_tokens")):
+        _need(t, name, (torch.int32,))
+    if parents.dim() != 2 or draft_tokens.shape != parents.shape or target_tokens.shape != parents.shape:
+        raise ValueError("parents / draft_tokens / target_tokens must share one [S, Q] shape")
+    s, q = parents.shape
+    dev = parents.device
+    if keep is None:
+        keep = torch.full((s, q), -1, dtype=torch.int32, device=dev)
+    if n_keep is None:
+        n_keep = torch.empty((s,), dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty((s,), dtype=torch.int32, device=dev)
+    _need(keep, "keep", (torch.int32,))
+    _need(n_keep, "n_keep", (torch.int32,))
+    _need(next_token, "next_token", (torch.int32,))
+    if status is not None:
+        _need(status, "status", (torch.int32,))
+    if keep.dim() != 2 or keep.shape[0] != s or n_keep.shape != (s,) or next_token.shape != (s,):
+        raise ValueError("output shape mismatch")
+    return s, q, keep, n_keep, next_token
+
+
+def tree_accept(parents, draft_tokens, target_tokens, *, keep=None, n_keep=None, next_token=None, status=None,
+                stream=None):
+    """``ddtree_tree_accept``: greedy acceptance; returns ``(keep [S, K], n_keep [S], next_token [S])``."""
+    s, q, keep, n_keep, next_token = _accept_inputs(parents, draft_tokens, target_tokens, keep, n_keep, next_token,
+                                                    status)
+    _check(LIB.ddtree_tree_accept(_ptr(parents), _ptr(draft_tokens), _ptr(target_tokens), int(q), int(s), _ptr(keep),
+                                  int(keep.shape[1]), _ptr(n_keep), _ptr(next_token), _ptr(status),
+                                  _stream(stream)))
+    return keep, n_keep, next_token
+
+
+def accept_compact(ckv, kpe, prefix_len: int, parents, draft_tokens, target_tokens, *, keep=None, n_keep=None,
+                   next_token=None, status=None, stream=None):
+    """``ddtree_accept_compact``: acceptance, then the in-place compaction of ``ckv`` / ``kpe``, in one
+    launch; returns ``(keep, n_keep, next_token)``."""
+    _need(ckv, "ckv", _BF16)
+    _need(kpe, "kpe", _BF16)
+    s, q, keep, n_keep, next_token = _accept_inputs(parents, draft_tokens, target_tokens, keep, n_keep, next_token,
+                                                    status)
+    rows = ckv.shape[1]
+    if ckv.shape[0] != s or kpe.shape[:2] != (s, rows):
+        raise ValueError("shape mismatch")
+    cache = KVCache(ckv.data_ptr(), kpe.data_ptr(), int(rows), int(s))
+    _check(LIB.ddtree_accept_compact(ctypes.byref(cache), int(prefix_len), _ptr(parents), _ptr(draft_tokens),
+                                     _ptr(target_tokens), int(q), _ptr(keep), int(keep.shape[1]), _ptr(n_keep),
+                                     _ptr(next_token), _ptr(status), _stream(stream)))
+    return keep, n_keep, next_token

@@ -302,3 +302,92 @@ int ddtree_compact_kv(const ddtree_kv_cache* cache, int prefix_len, const int32_
 }
 
 }  // extern "C"
+
+namespace {
+
+// Shared argument checks of the acceptance calls.  Returns DDTREE_OK or an error code.
+int check_accept(const int32_t* parents, const int32_t* draft_tokens, const int32_t* target_tokens, int q_len,
+                 int n_streams, int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
+                 int32_t* dev_status) {
+  if (!parents || !draft_tokens || !target_tokens || !keep || !n_keep) return DDTREE_ERR_NULL;
+  if (q_len < 1 || q_len > kMaxQ || n_streams < 1 || keep_stride < q_len) return DDTREE_ERR_SHAPE;
+  if (!aligned4(parents) || !aligned4(draft_tokens) || !aligned4(target_tokens) || !aligned4(keep) ||
+      !aligned4(n_keep) || (next_token && !aligned4(next_token)) || (dev_status && !aligned4(dev_status)))
+    return DDTREE_ERR_ALIGN;
+  const size_t in_bytes = (size_t)n_streams * q_len * 4;
+  const Range ins[3] = {range_of(parents, in_bytes), range_of(draft_tokens, in_bytes), range_of(target_tokens, in_bytes)};
+  Range outs[3] = {range_of(keep, (size_t)n_streams * keep_stride * 4), range_of(n_keep, (size_t)n_streams * 4),
+                   range_of(next_token, next_token ? (size_t)n_streams * 4 : 0)};
+  const int n_out = next_token ? 3 : 2;
+  for (int o = 0; o < n_out; ++o) {
+    for (const Range& r : ins)
+      if (overlap(outs[o], r)) return DDTREE_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < n_out; ++o2)
+      if (overlap(outs[o], outs[o2])) return DDTREE_ERR_ALIAS;
+  }
+  return DDTREE_OK;
+}
+
+ddtree::AcceptArgs accept_args(const int32_t* parents, const int32_t* draft_tokens, const int32_t* target_tokens,
+                               int q_len, int n_streams, int32_t* keep, int keep_stride, int32_t* n_keep,
+                               int32_t* next_token, int32_t* dev_status) {
+  ddtree::AcceptArgs a{};
+  a.parents = parents;
+  a.draft = draft_tokens;
+  a.target = target_tokens;
+  a.keep = keep;
+  a.n_keep = n_keep;
+  a.next_token = next_token;
+  a.status = dev_status;
+  a.q_len = q_len;
+  a.n_streams = n_streams;
+  a.keep_stride = keep_stride;
+  return a;
+}
+
+}  // namespace
+
+int ddtree_tree_accept(const int32_t* parents, const int32_t* draft_tokens, const int32_t* target_tokens,
+                       int q_len, int n_streams, int32_t* keep, int keep_stride, int32_t* n_keep,
+                       int32_t* next_token, int32_t* dev_status, hipStream_t stream) {
+  const int rc = check_accept(parents, draft_tokens, target_tokens, q_len, n_streams, keep, keep_stride, n_keep,
+                              next_token, dev_status);
+  if (rc != DDTREE_OK) return rc;
+  const ddtree::AcceptArgs a = accept_args(parents, draft_tokens, target_tokens, q_len, n_streams, keep,
+                                           keep_stride, n_keep, next_token, dev_status);
+  if (ddtree::launch_accept(a, stream) != hipSuccess) return DDTREE_ERR_HIP;
+  return DDTREE_OK;
+}
+
+int ddtree_accept_compact(const ddtree_kv_cache* cache, int prefix_len, const int32_t* parents,
+                          const int32_t* draft_tokens, const int32_t* target_tokens, int q_len,
+                          int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
+                          int32_t* dev_status, hipStream_t stream) {
+  if (!cache || !cache->ckv || !cache->kpe) return DDTREE_ERR_NULL;
+  int rc = check_accept(parents, draft_tokens, target_tokens, q_len, cache->n_streams, keep, keep_stride,
+                        n_keep, next_token, dev_status);
+  if (rc != DDTREE_OK) return rc;
+  if (cache->n_streams < 1 || cache->kv_rows < 1 || prefix_len < 0 ||
+      (long long)prefix_len + q_len > (long long)cache->kv_rows)
+    return DDTREE_ERR_SHAPE;
+  if (!aligned16(cache->ckv) || !aligned16(cache->kpe)) return DDTREE_ERR_ALIGN;
+  const Range ckv = range_of(cache->ckv, (size_t)cache->n_streams * cache->kv_rows * kDLat * 2);
+  const Range kpe = range_of(cache->kpe, (size_t)cache->n_streams * cache->kv_rows * kDRope * 2);
+  if (overlap(ckv, kpe)) return DDTREE_ERR_ALIAS;
+  const size_t in_bytes = (size_t)cache->n_streams * q_len * 4;
+  const Range others[6] = {range_of(parents, in_bytes), range_of(draft_tokens, in_bytes),
+                           range_of(target_tokens, in_bytes),
+                           range_of(keep, (size_t)cache->n_streams * keep_stride * 4),
+                           range_of(n_keep, (size_t)cache->n_streams * 4),
+                           range_of(next_token, next_token ? (size_t)cache->n_streams * 4 : 0)};
+  for (const Range& r : others)
+    if (overlap(r, ckv) || overlap(r, kpe)) return DDTREE_ERR_ALIAS;
+  ddtree::AcceptArgs a = accept_args(parents, draft_tokens, target_tokens, q_len, cache->n_streams, keep,
+                                     keep_stride, n_keep, next_token, dev_status);
+  a.ckv = static_cast<uint16_t*>(cache->ckv);
+  a.kpe = static_cast<uint16_t*>(cache->kpe);
+  a.kv_rows = cache->kv_rows;
+  a.prefix_len = prefix_len;
+  if (ddtree::launch_accept_compact(a, stream) != hipSuccess) return DDTREE_ERR_HIP;
+  return DDTREE_OK;
+}

@@ -75,4 +75,24 @@ struct CompactArgs {
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
 
+struct AcceptArgs {
+  const int32_t* parents;  // [n_streams][q_len]
+  const int32_t* draft;    // [n_streams][q_len]
+  const int32_t* target;   // [n_streams][q_len]
+  int32_t* keep;           // [n_streams][keep_stride]
+  int32_t* n_keep;         // [n_streams]
+  int32_t* next_token;     // [n_streams] or null
+  int32_t* status;         // or null
+  uint16_t* ckv;           // fused compaction only
+  uint16_t* kpe;
+  int kv_rows;
+  int prefix_len;
+  int q_len;
+  int n_streams;
+  int keep_stride;
+};
+
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+hipError_t launch_accept_compact(const AcceptArgs& a, hipStream_t stream);
+
 }  // namespace ddtree
