@@ -1,12 +1,15 @@
-"""Benchmark: tree-verify MLA-absorb attention + KV compaction on one MI355X.
+"""Benchmark: tree-verify MLA-absorb attention, greedy acceptance and KV compaction on one MI355X.
 
 One step = one pass of the whole hot path over one batch: ``ddtree_verify_attn_ex`` (64 heads,
-latent 512 + rope 64, tree mask from parents[]) followed by ``ddtree_compact_kv`` of each
-stream's accepted root-to-leaf path.  Inputs are seeded synthetic bf16 ~ N(0,1) (no dataset is
-involved) and are resident in HBM before the timed region starts.
+latent 512 + rope 64, tree mask from parents[]) followed by ``ddtree_accept_compact`` (greedy
+acceptance of each stream's tree against synthetic target tokens, then the in-place compaction
+of the accepted root-to-leaf path, one launch).  Inputs are seeded synthetic bf16 ~ N(0,1) and
+token ids (no dataset is involved) and are resident in HBM before the timed region starts.
 
 Prints one JSON line.  ``value`` is TFLOP/s of the verify attention counted over visible
-(query, key) pairs only, divided by the whole step time (verify + compaction).
+(query, key) pairs only, divided by the whole step time (verify + accept + compaction).  The
+``detail`` object also carries per-call times of ``ddtree_tree_accept`` over the stream and
+budget grid the pages report, of the fused call, and of ``ddtree_compact_kv`` alone.
 """
 from __future__ import annotations
 
@@ -87,6 +90,53 @@ def cpu_baseline(w, flops_per_stream: float, budget_s: float = 12.0):
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"fp64 oracle on streams 0..{done - 1} of {w.streams} of workload {w.name} "
                       f"({t_total:.1f} s)"}
+
+
+def time_calls(fn, n: int = 100, replays: int = 5) -> float:
+    """Microseconds per call of ``fn`` on the GPU: ``n`` calls captured in one HIP graph (so the
+    host's per-call overhead drops out), replayed ``replays`` times, best replay."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(replays):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) / n * 1e3)
+    return best
+
+
+def accept_table(lib, dev):
+    """``ddtree_tree_accept`` us/call for 1, 8, 64 streams and budgets 8, 32 (q_len 9, 33)."""
+    import torch
+    import synth
+    table = {}
+    for streams in (1, 8, 64):
+        for q in (9, 33):
+            cases = [synth.accept_case(90 + q, s, q) for s in range(streams)]
+            par = torch.from_numpy(np.stack([c[0] for c in cases]).astype(np.int32)).to(dev)
+            dr = torch.from_numpy(np.stack([c[1] for c in cases]).astype(np.int32)).to(dev)
+            tg = torch.from_numpy(np.stack([c[2] for c in cases]).astype(np.int32)).to(dev)
+            keep = torch.empty((streams, q), dtype=torch.int32, device=dev)
+            n_keep = torch.empty((streams,), dtype=torch.int32, device=dev)
+            nxt = torch.empty((streams,), dtype=torch.int32, device=dev)
+            us = time_calls(lambda: lib.tree_accept(par, dr, tg, keep=keep, n_keep=n_keep, next_token=nxt))
+            table[f"streams{streams}_budget{q - 1}"] = round(us, 2)
+    return table
 
 
 def _db_rows(path: str, sql: str):
@@ -202,8 +252,11 @@ def main() -> int:
 
     q_lat, q_pe, ckv, kpe = up(b.q_lat), up(b.q_pe), up(b.ckv), up(b.kpe)
     parents = torch.from_numpy(b.parents).to(dev)
+    draft_tok = torch.from_numpy(b.draft_tok).to(dev)
+    target_tok = torch.from_numpy(b.target_tok).to(dev)
     keep = torch.from_numpy(b.keep).to(dev)
     n_keep = torch.from_numpy(b.n_keep).to(dev)
+    next_tok = torch.empty((w.streams,), dtype=torch.int32, device=dev)
     out = torch.empty((w.streams, w.q_len, w.heads, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((w.streams, w.q_len, w.heads), dtype=torch.float32, device=dev)
     splits = _lib.num_splits(w.prefix, w.q_len, w.streams, args.num_splits)
@@ -220,7 +273,8 @@ def main() -> int:
                             num_splits=args.num_splits, workspace=ws, stream=stream)
         if ev_b is not None:
             ev_b.record(stream)
-        _lib.compact_kv(ckv, kpe, w.prefix, keep, n_keep, stream=stream)
+        _lib.accept_compact(ckv, kpe, w.prefix, parents, draft_tok, target_tok, keep=keep, n_keep=n_keep,
+                            next_token=next_tok, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -238,6 +292,12 @@ def main() -> int:
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / args.steps
     verify_ms = float(np.mean([a.elapsed_time(bb) for a, bb in evs]))
+
+    # per-call times of the acceptance and compaction entry points (outside the timed steps)
+    accept_us = accept_table(_lib, dev)
+    fused_us = time_calls(lambda: _lib.accept_compact(ckv, kpe, w.prefix, parents, draft_tok, target_tok, keep=keep,
+                                                      n_keep=n_keep, next_token=next_tok))
+    compact_us = time_calls(lambda: _lib.compact_kv(ckv, kpe, w.prefix, keep, n_keep))
 
     flops = 2.0 * w.heads * (576 + 512) * visible_pairs(b.parents, w.prefix)
     tflops_step = flops / (ms_step * 1e-3) / 1e12
@@ -258,11 +318,14 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "streams": w.streams, "heads": w.heads, "prefix": w.prefix,
                    "q_len": w.q_len, "tree": w.tree, "seed": w.seed, "num_splits": splits,
-                   "step": "verify_attn + compact_kv"},
+                   "step": "verify_attn + accept_compact"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "detail": {"verify_us_per_call": round(verify_ms * 1e3, 2),
-                   "compact_us_per_call_incl_gap": round((ms_step - verify_ms) * 1e3, 2),
+                   "accept_compact_us_per_call_incl_gap": round((ms_step - verify_ms) * 1e3, 2),
+                   "accept_compact_us_per_call": round(fused_us, 2),
+                   "compact_kv_us_per_call": round(compact_us, 2),
+                   "tree_accept_us_per_call": accept_us,
                    "verify_tflops": round(achieved, 2),
                    "pct_mfma_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
                    "algorithmic_bytes": algorithmic_bytes(w, w.streams),
