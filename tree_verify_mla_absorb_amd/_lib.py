@@ -16,13 +16,13 @@ LIB_PATH = os.path.join(_HERE, "libddtree.so")
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = -1, -2, -3, -4, -5, -6
-STATUS_BAD_PARENTS, STATUS_BAD_KEEP = 1, 2
+STATUS_BAD_PARENTS, STATUS_BAD_KEEP, STATUS_BAD_PREFIX = 1, 2, 4
 HEADS, D_LATENT, D_ROPE, MAX_Q_LEN = 64, 512, 64, 64
 
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m tree_verify_mla_absorb_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python tree_verify_mla_absorb_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.ddtree_verify_attn.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, vp]
@@ -40,6 +40,13 @@ def _load() -> ctypes.CDLL:
     lib.ddtree_tree_accept.restype = i32
     lib.ddtree_accept_compact.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp]
     lib.ddtree_accept_compact.restype = i32
+    lib.ddtree_verify_attn_ragged.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, i32, f32, i32, vp, sz,
+                                              vp, vp]
+    lib.ddtree_verify_attn_ragged.restype = i32
+    lib.ddtree_compact_kv_ragged.argtypes = [vp, vp, vp, vp, i32, vp, vp]
+    lib.ddtree_compact_kv_ragged.restype = i32
+    lib.ddtree_accept_compact_ragged.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp]
+    lib.ddtree_accept_compact_ragged.restype = i32
     lib.ddtree_status_string.argtypes = [i32]
     lib.ddtree_status_string.restype = ctypes.c_char_p
     lib.ddtree_version.argtypes = []
@@ -57,6 +64,9 @@ EXPORTED = (
     "ddtree_compact_kv",
     "ddtree_tree_accept",
     "ddtree_accept_compact",
+    "ddtree_verify_attn_ragged",
+    "ddtree_compact_kv_ragged",
+    "ddtree_accept_compact_ragged",
     "ddtree_status_string",
     "ddtree_version",
 )
@@ -173,6 +183,45 @@ def verify_attn_ex(q_lat, q_pe, ckv, kpe, prefix_len: int, parents, *, out=None,
     return out, lse
 
 
+def verify_attn_ragged(q_lat, q_pe, ckv, kpe, prefix_lens, max_prefix_len: int, parents, *, out=None, lse=None,
+                       scale: float = 0.0, num_splits: int = 0, workspace=None, status=None, stream=None):
+    """``ddtree_verify_attn_ragged``: ``prefix_lens`` is a device int32 ``[S]`` tensor bounded by
+    ``max_prefix_len``.  ``workspace`` is allocated here when needed and not given."""
+    s, q, rows = _shapes(q_lat, q_pe, ckv, kpe, parents)
+    _need(prefix_lens, "prefix_lens", (torch.int32,))
+    if prefix_lens.shape != (s,):
+        raise ValueError("prefix_lens must be [S]")
+    out, lse = _outputs(q_lat, out, lse)
+    need = workspace_size(max_prefix_len, q, s, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if status is not None:
+        _need(status, "status", (torch.int32,))
+    _check(LIB.ddtree_verify_attn_ragged(_ptr(q_lat), _ptr(q_pe), _ptr(ckv), _ptr(kpe), _ptr(prefix_lens),
+                                         int(max_prefix_len), _ptr(parents), int(q), int(s), _ptr(out), _ptr(lse),
+                                         int(rows), float(scale), int(num_splits), _ptr(workspace), nbytes,
+                                         _ptr(status), _stream(stream)))
+    return out, lse
+
+
+def compact_kv_ragged(ckv, kpe, prefix_lens, keep, n_keep, *, status=None, stream=None) -> None:
+    """``ddtree_compact_kv_ragged`` in place; ``prefix_lens`` device int32 ``[S]``."""
+    _need(ckv, "ckv", _BF16)
+    _need(kpe, "kpe", _BF16)
+    for t, name in ((prefix_lens, "prefix_lens"), (keep, "keep"), (n_keep, "n_keep")):
+        _need(t, name, (torch.int32,))
+    if status is not None:
+        _need(status, "status", (torch.int32,))
+    s, rows = ckv.shape[0], ckv.shape[1]
+    if kpe.shape[:2] != (s, rows) or keep.dim() != 2 or keep.shape[0] != s or n_keep.shape != (s,) \
+            or prefix_lens.shape != (s,):
+        raise ValueError("shape mismatch")
+    cache = KVCache(ckv.data_ptr(), kpe.data_ptr(), int(rows), int(s))
+    _check(LIB.ddtree_compact_kv_ragged(ctypes.byref(cache), _ptr(prefix_lens), _ptr(keep), _ptr(n_keep),
+                                        int(keep.shape[1]), _ptr(status), _stream(stream)))
+
+
 def compact_kv(ckv, kpe, prefix_len: int, keep, n_keep, *, status=None, stream=None) -> None:
     """``ddtree_compact_kv`` in place on ``ckv [S, rows, 512]`` / ``kpe [S, rows, 64]``."""
     _need(ckv, "ckv", _BF16)
@@ -238,4 +287,24 @@ def accept_compact(ckv, kpe, prefix_len: int, parents, draft_tokens, target_toke
     _check(LIB.ddtree_accept_compact(ctypes.byref(cache), int(prefix_len), _ptr(parents), _ptr(draft_tokens),
                                      _ptr(target_tokens), int(q), _ptr(keep), int(keep.shape[1]), _ptr(n_keep),
                                      _ptr(next_token), _ptr(status), _stream(stream)))
+    return keep, n_keep, next_token
+
+
+def accept_compact_ragged(ckv, kpe, prefix_lens, parents, draft_tokens, target_tokens, *, keep=None, n_keep=None,
+                          next_token=None, status=None, stream=None):
+    """``ddtree_accept_compact_ragged``: like ``accept_compact`` with a device int32 ``[S]``
+    ``prefix_lens``, which the call advances by each stream's accepted count."""
+    _need(ckv, "ckv", _BF16)
+    _need(kpe, "kpe", _BF16)
+    _need(prefix_lens, "prefix_lens", (torch.int32,))
+    s, q, keep, n_keep, next_token = _accept_inputs(parents, draft_tokens, target_tokens, keep, n_keep, next_token,
+                                                    status)
+    rows = ckv.shape[1]
+    if ckv.shape[0] != s or kpe.shape[:2] != (s, rows) or prefix_lens.shape != (s,):
+        raise ValueError("shape mismatch")
+    cache = KVCache(ckv.data_ptr(), kpe.data_ptr(), int(rows), int(s))
+    _check(LIB.ddtree_accept_compact_ragged(ctypes.byref(cache), _ptr(prefix_lens), _ptr(parents),
+                                            _ptr(draft_tokens), _ptr(target_tokens), int(q), _ptr(keep),
+                                            int(keep.shape[1]), _ptr(n_keep), _ptr(next_token), _ptr(status),
+                                            _stream(stream)))
     return keep, n_keep, next_token

@@ -1,6 +1,8 @@
 """Build ``libddtree.so`` in-tree with hipcc for gfx950 only.
 
-    python -m tree_verify_mla_absorb_amd.build
+    python tree_verify_mla_absorb_amd/build.py
+
+(Run it as a script: importing the package loads the library, which may not exist yet.)
 
 The library is a plain C-ABI shared object (``include/ddtree.h``); it links against the HIP
 runtime only.  Every HIP source is compiled with packed-fp32 instruction selection turned off.
