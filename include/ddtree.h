@@ -64,6 +64,7 @@ extern "C" {
 #define DDTREE_STATUS_BAD_PARENTS 1 /* a parents[] entry is not an earlier node; that node's
                                        ancestor walk stops there                               */
 #define DDTREE_STATUS_BAD_KEEP 2    /* keep[]/n_keep of a stream invalid; that stream untouched */
+#define DDTREE_STATUS_BAD_PREFIX 4  /* a per-stream prefix length out of range; see the ragged calls */
 
 /*
  * ddtree_verify_attn -- tree-verify attention, absorbed MLA form, one launch for all streams.
@@ -200,6 +201,52 @@ int ddtree_accept_compact(const ddtree_kv_cache* cache, int prefix_len, const in
                           const int32_t* draft_tokens, const int32_t* target_tokens, int q_len,
                           int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
                           int32_t* dev_status, hipStream_t stream);
+
+/*
+ * Per-stream (ragged) prefix lengths.  After compaction every stream's committed prefix grows by
+ * its own accepted count, so the streams of a batch soon hold different prefix lengths.  These
+ * calls take them as a device array prefix_lens [n_streams] (int32, 4-byte aligned); stream s's
+ * tree block is at rows [prefix_lens[s], prefix_lens[s] + q_len) of its cache rows.  A value the
+ * device finds out of range sets DDTREE_STATUS_BAD_PREFIX in dev_status (when given).
+ */
+
+/*
+ * ddtree_verify_attn_ragged -- ddtree_verify_attn_ex with prefix_lens instead of one prefix_len.
+ *   max_prefix_len  host bound: 0 <= prefix_lens[s] <= max_prefix_len for every stream; the launch,
+ *                   the split plan and the workspace (ddtree_verify_attn_workspace_size with
+ *                   max_prefix_len) are sized for it, and kv_rows >= max_prefix_len + q_len.
+ * A stream whose prefix_lens entry is outside [0, max_prefix_len] gets NaN in out_lat and lse and
+ * sets DDTREE_STATUS_BAD_PREFIX; the other streams are unaffected.  Shorter streams leave part
+ * of the launch idle; all results are those of ddtree_verify_attn_ex with that stream's prefix.
+ */
+int ddtree_verify_attn_ragged(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
+                              const int32_t* prefix_lens, int max_prefix_len, const int32_t* parents,
+                              int q_len, int n_streams, float* out_lat, float* lse, int kv_rows,
+                              float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                              int32_t* dev_status, hipStream_t stream);
+
+/*
+ * ddtree_compact_kv_ragged -- ddtree_compact_kv with prefix_lens (read only) instead of one
+ * prefix_len.  A stream whose prefix_lens entry is negative or above kv_rows is skipped and flagged
+ * (DDTREE_STATUS_BAD_PREFIX); keep entries are checked against that stream's own prefix.
+ */
+int ddtree_compact_kv_ragged(const ddtree_kv_cache* cache, const int32_t* prefix_lens, const int32_t* keep,
+                             const int32_t* n_keep, int keep_stride, int32_t* dev_status,
+                             hipStream_t stream);
+
+/*
+ * ddtree_accept_compact_ragged -- ddtree_accept_compact with prefix_lens, which it also ADVANCES:
+ * for every stream whose compaction ran, prefix_lens[s] += n_keep[s] (the accepted rows are now
+ * committed and the next tree goes right after them).  So verify -> accept -> compact -> the next
+ * verify run on the device without a host round trip.  A stream with
+ * prefix_lens[s] + q_len > kv_rows (or a negative entry) keeps its cache and prefix unchanged and
+ * sets DDTREE_STATUS_BAD_PREFIX; its keep / n_keep / next_token are still written.
+ * Requires q_len <= cache->kv_rows.
+ */
+int ddtree_accept_compact_ragged(const ddtree_kv_cache* cache, int32_t* prefix_lens, const int32_t* parents,
+                                 const int32_t* draft_tokens, const int32_t* target_tokens, int q_len,
+                                 int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
+                                 int32_t* dev_status, hipStream_t stream);
 
 /* Static text for a return code. */
 const char* ddtree_status_string(int code);

@@ -23,8 +23,9 @@ from .verify import (  # noqa: F401
     scores_absorbed,
     verify_attn,
     verify_attn_f64,
+    verify_attn_ragged,
     verify_attn_stream,
     visibility,
 )
-from .compact import compact_kv, validate_keep  # noqa: F401
+from .compact import compact_kv, compact_kv_ragged, validate_keep  # noqa: F401
 from .accept import tree_accept, tree_accept_streams, validate_parents  # noqa: F401

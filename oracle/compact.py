@@ -48,3 +48,16 @@ def compact_kv(ckv_bits: np.ndarray, kpe_bits: np.ndarray, prefix_len: int, keep
         new_c[s, prefix_len:prefix_len + n] = old_c[s, src]
         new_k[s, prefix_len:prefix_len + n] = old_k[s, src]
     return new_c, new_k
+
+
+def compact_kv_ragged(ckv_bits: np.ndarray, kpe_bits: np.ndarray, prefix_lens, keep: np.ndarray,
+                      n_keep: np.ndarray):
+    """``compact_kv`` with a prefix length per stream: for every stream ``s`` and
+    ``i < n_keep[s]``, row ``prefix_lens[s] + i`` takes the old row ``prefix_lens[s] + keep[s, i]``."""
+    new_c = np.array(ckv_bits, copy=True)
+    new_k = np.array(kpe_bits, copy=True)
+    for s in range(new_c.shape[0]):
+        c, k = compact_kv(ckv_bits[s:s + 1], kpe_bits[s:s + 1], int(prefix_lens[s]), keep[s:s + 1],
+                          n_keep[s:s + 1])
+        new_c[s], new_k[s] = c[0], k[0]
+    return new_c, new_k

@@ -135,3 +135,23 @@ def verify_attn(q_lat_bits, q_pe_bits, ckv_bits, kpe_bits, prefix_len: int, pare
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
+
+
+def verify_attn_ragged(q_lat_bits, q_pe_bits, ckv_bits, kpe_bits, prefix_lens, parents,
+                       scale: float = DEFAULT_SCALE):
+    """Streams with their own prefix lengths: stream ``s`` is ``verify_attn_stream`` with
+    ``prefix_lens[s]`` (its tree block at rows ``[prefix_lens[s], prefix_lens[s] + Q)``).
+
+    After compaction each stream's committed prefix grows by its own accepted count ("Race
+    Conditions, Buffer Aliasing, and the Architecture of a Native DDTree Inference Engine",
+    section "The Cache Compaction Problem": the accepted rows join the prefix), so streams of one
+    batch hold different prefix lengths.
+    """
+    parents = np.asarray(parents)
+    outs, lses = [], []
+    for s in range(parents.shape[0]):
+        o, l = verify_attn_stream(q_lat_bits[s], q_pe_bits[s], ckv_bits[s], kpe_bits[s],
+                                  int(prefix_lens[s]), parents[s], scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)

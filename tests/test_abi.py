@@ -163,3 +163,22 @@ def test_accept_compact_argument_errors():
     assert accept_compact(prefix=292) == _lib.ERR_SHAPE   # tree block past the cache rows
     assert accept_compact(s=0) == _lib.ERR_SHAPE
     assert accept_compact(keep=G + 64) == _lib.ERR_ALIAS  # keep inside the latent cache
+
+
+def test_ragged_argument_errors():
+    L = _lib.LIB
+    # verify: prefix_lens is required; max_prefix_len bounds kv_rows like prefix_len does
+    assert L.ddtree_verify_attn_ragged(A, B, C, D, None, 100, E, 9, 2, F, G, 109, 0.0, 1, None, 0, None,
+                                       None) == _lib.ERR_NULL
+    assert L.ddtree_verify_attn_ragged(A, B, C, D, 0xE0000000, 100, E, 9, 2, F, G, 108, 0.0, 1, None, 0, None,
+                                       None) == _lib.ERR_SHAPE
+    assert L.ddtree_verify_attn_ragged(A, B, C, D, 0xE0000002, 100, E, 9, 2, F, G, 109, 0.0, 1, None, 0, None,
+                                       None) == _lib.ERR_ALIGN
+    assert L.ddtree_verify_attn_ragged(A, B, C, D, F, 100, E, 9, 2, F, G, 109, 0.0, 1, None, 0, None,
+                                       None) == _lib.ERR_ALIAS  # prefix_lens over out
+    c = _lib.KVCache(G, G + 0x10000000, 300, 2)
+    assert L.ddtree_compact_kv_ragged(ctypes.byref(c), None, E, F, 9, None, None) == _lib.ERR_NULL
+    assert L.ddtree_compact_kv_ragged(ctypes.byref(c), G + 64, E, F, 9, None, None) == _lib.ERR_ALIAS
+    assert L.ddtree_accept_compact_ragged(ctypes.byref(c), None, A, B, C, 9, D, 9, E, F, None, None) == _lib.ERR_NULL
+    assert L.ddtree_accept_compact_ragged(ctypes.byref(c), D + 8, A, B, C, 9, D, 9, E, F, None,
+                                          None) == _lib.ERR_ALIAS  # prefix_lens inside keep

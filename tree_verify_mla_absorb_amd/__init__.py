@@ -8,12 +8,15 @@ The compute lives in ``libddtree.so`` (C ABI, ``include/ddtree.h``); this packag
 from ._lib import (  # noqa: F401
     DDTreeError,
     accept_compact,
+    accept_compact_ragged,
     compact_kv,
+    compact_kv_ragged,
     num_splits,
     status_string,
     tree_accept,
     verify_attn,
     verify_attn_ex,
+    verify_attn_ragged,
     version,
     workspace_size,
 )

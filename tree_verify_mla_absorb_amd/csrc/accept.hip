@@ -71,12 +71,15 @@ __global__ void __launch_bounds__(64) tree_accept_kernel(AcceptArgs a) {
   write_outputs(a, s, lane, w);
 }
 
-// One workgroup per stream: wave 0 walks, then all waves gather the accepted rows.
+// One workgroup per stream: wave 0 walks, then all waves gather the accepted rows.  With
+// per-stream prefix lengths, the stream's entry is then advanced by the accepted count: the
+// accepted rows are committed, and the next tree goes after them.
 __global__ void __launch_bounds__(kCompactThreads) accept_compact_kernel(AcceptArgs a) {
   __shared__ int keep_s[kMaxQ];
   __shared__ int n_s;
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
+  const int P = a.prefix_lens != nullptr ? a.prefix_lens[s] : a.prefix_len;
   if (tid < 64) {
     const Walk w = accept_walk(a, s, tid);
     write_outputs(a, s, tid, w);
@@ -86,7 +89,12 @@ __global__ void __launch_bounds__(kCompactThreads) accept_compact_kernel(AcceptA
   __syncthreads();
   const int n = n_s;
   if (n == 0) return;  // malformed tree: the cache is left untouched
-  compact_rows(a.ckv, a.kpe, (size_t)s * a.kv_rows + a.prefix_len, keep_s, n);
+  if (P < 0 || (long long)P + a.q_len > (long long)a.kv_rows) {  // uniform over the workgroup
+    if (tid == 0 && a.status != nullptr) atomicOr(a.status, DDTREE_STATUS_BAD_PREFIX);
+    return;
+  }
+  compact_rows(a.ckv, a.kpe, (size_t)s * a.kv_rows + P, keep_s, n);
+  if (a.prefix_lens != nullptr && tid == 0) a.prefix_lens[s] = P + n;
 }
 
 }  // namespace

@@ -21,10 +21,15 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kv_kernel(CompactArgs
     if (tid == 0 && a.status != nullptr) atomicOr(a.status, DDTREE_STATUS_BAD_KEEP);
     return;
   }
+  const int P = a.prefix_lens != nullptr ? a.prefix_lens[s] : a.prefix_len;
+  if (P < 0 || P > a.kv_rows) {  // uniform over the workgroup
+    if (tid == 0 && a.status != nullptr) atomicOr(a.status, DDTREE_STATUS_BAD_PREFIX);
+    return;
+  }
   if (tid < n) {
     const int32_t* kp = a.keep + (size_t)s * a.keep_stride;
     const int k = kp[tid];
-    bool ok = k >= 0 && (long long)a.prefix_len + k < (long long)a.kv_rows;
+    bool ok = k >= 0 && (long long)P + k < (long long)a.kv_rows;
     if (tid > 0) ok = ok && kp[tid - 1] < k;
     keep_s[tid] = k;
     if (!ok) bad_s = 1;
@@ -35,7 +40,7 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kv_kernel(CompactArgs
     return;
   }
 
-  compact_rows(a.ckv, a.kpe, (size_t)s * a.kv_rows + a.prefix_len, keep_s, n);
+  compact_rows(a.ckv, a.kpe, (size_t)s * a.kv_rows + P, keep_s, n);
 }
 
 }  // namespace

@@ -181,16 +181,20 @@ size_t ddtree_verify_attn_workspace_size(int prefix_len, int q_len, int n_stream
   return workspace_bytes_for(make_plan(prefix_len, q_len, n_streams, num_splits));
 }
 
-int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
-                          int prefix_len, const int32_t* parents, int q_len, int n_streams,
-                          float* out_lat, float* lse, int kv_rows, float scale, int num_splits,
-                          void* workspace, size_t workspace_bytes, int32_t* dev_status,
-                          hipStream_t stream) {
+namespace {
+
+// ddtree_verify_attn_ex and ddtree_verify_attn_ragged: prefix_lens == nullptr means every stream
+// has prefix_len rows of prefix; otherwise prefix_len bounds the per-stream device values.
+int verify_impl(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe, int prefix_len,
+                const int32_t* prefix_lens, const int32_t* parents, int q_len, int n_streams, float* out_lat,
+                float* lse, int kv_rows, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                int32_t* dev_status, hipStream_t stream) {
   if (!q_lat || !q_pe || !ckv || !kpe || !parents || !out_lat || !lse) return DDTREE_ERR_NULL;
   if (!shape_ok(prefix_len, q_len, n_streams) || num_splits < 0) return DDTREE_ERR_SHAPE;
   if (kv_rows < prefix_len + q_len) return DDTREE_ERR_SHAPE;
   if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(ckv) || !aligned16(kpe) || !aligned16(out_lat) ||
-      !aligned4(lse) || !aligned4(parents) || (dev_status && !aligned4(dev_status)))
+      !aligned4(lse) || !aligned4(parents) || (dev_status && !aligned4(dev_status)) ||
+      (prefix_lens && !aligned4(prefix_lens)))
     return DDTREE_ERR_ALIGN;
   if (kv_rows > (1 << 21)) return DDTREE_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) scale = 1.0f / sqrtf(192.0f);
@@ -202,7 +206,8 @@ int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, 
       range_of(q_lat, rows_q * kDLat * 2), range_of(q_pe, rows_q * kDRope * 2),
       range_of(ckv, (size_t)n_streams * kv_rows * kDLat * 2),
       range_of(kpe, (size_t)n_streams * kv_rows * kDRope * 2),
-      range_of(parents, (size_t)n_streams * q_len * sizeof(int32_t))};
+      range_of(parents, (size_t)n_streams * q_len * sizeof(int32_t)),
+      range_of(prefix_lens, prefix_lens ? (size_t)n_streams * sizeof(int32_t) : 0)};
   for (const Range& in : inputs)
     if (overlap(in, r_out) || overlap(in, r_lse)) return DDTREE_ERR_ALIAS;
   if (overlap(r_out, r_lse)) return DDTREE_ERR_ALIAS;
@@ -220,6 +225,7 @@ int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, 
   a.out = out_lat;
   a.lse = lse;
   a.status = dev_status;
+  a.prefix_lens = prefix_lens;
   a.prefix_len = prefix_len;
   a.q_len = q_len;
   a.n_streams = n_streams;
@@ -268,6 +274,27 @@ int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, 
   return DDTREE_OK;
 }
 
+}  // namespace
+
+int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
+                          int prefix_len, const int32_t* parents, int q_len, int n_streams,
+                          float* out_lat, float* lse, int kv_rows, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                          hipStream_t stream) {
+  return verify_impl(q_lat, q_pe, ckv, kpe, prefix_len, nullptr, parents, q_len, n_streams, out_lat, lse, kv_rows,
+                     scale, num_splits, workspace, workspace_bytes, dev_status, stream);
+}
+
+int ddtree_verify_attn_ragged(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
+                              const int32_t* prefix_lens, int max_prefix_len, const int32_t* parents, int q_len,
+                              int n_streams, float* out_lat, float* lse, int kv_rows, float scale,
+                              int num_splits, void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                              hipStream_t stream) {
+  if (!prefix_lens) return DDTREE_ERR_NULL;
+  return verify_impl(q_lat, q_pe, ckv, kpe, max_prefix_len, prefix_lens, parents, q_len, n_streams, out_lat, lse,
+                     kv_rows, scale, num_splits, workspace, workspace_bytes, dev_status, stream);
+}
+
 int ddtree_verify_attn(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
                        int prefix_len, const int32_t* parents, int q_len, int n_streams,
                        float* out_lat, float* lse, hipStream_t stream) {
@@ -275,30 +302,51 @@ int ddtree_verify_attn(const void* q_lat, const void* q_pe, const void* ckv, con
                                prefix_len + q_len, 0.f, 1, nullptr, 0, nullptr, stream);
 }
 
-int ddtree_compact_kv(const ddtree_kv_cache* cache, int prefix_len, const int32_t* keep,
-                      const int32_t* n_keep, int keep_stride, int32_t* dev_status, hipStream_t stream) {
+namespace {
+
+int compact_impl(const ddtree_kv_cache* cache, int prefix_len, const int32_t* prefix_lens, const int32_t* keep,
+                 const int32_t* n_keep, int keep_stride, int32_t* dev_status, hipStream_t stream) {
   if (!cache || !cache->ckv || !cache->kpe || !keep || !n_keep) return DDTREE_ERR_NULL;
   if (cache->n_streams < 1 || cache->kv_rows < 1 || prefix_len < 0 || prefix_len > cache->kv_rows ||
       keep_stride < 1)
     return DDTREE_ERR_SHAPE;
   if (!aligned16(cache->ckv) || !aligned16(cache->kpe) || !aligned4(keep) || !aligned4(n_keep) ||
-      (dev_status && !aligned4(dev_status)))
+      (dev_status && !aligned4(dev_status)) || (prefix_lens && !aligned4(prefix_lens)))
     return DDTREE_ERR_ALIGN;
-  if (overlap(range_of(cache->ckv, (size_t)cache->n_streams * cache->kv_rows * kDLat * 2),
-              range_of(cache->kpe, (size_t)cache->n_streams * cache->kv_rows * kDRope * 2)))
-    return DDTREE_ERR_ALIAS;
+  const Range ckv = range_of(cache->ckv, (size_t)cache->n_streams * cache->kv_rows * kDLat * 2);
+  const Range kpe = range_of(cache->kpe, (size_t)cache->n_streams * cache->kv_rows * kDRope * 2);
+  if (overlap(ckv, kpe)) return DDTREE_ERR_ALIAS;
+  const Range small[3] = {range_of(keep, (size_t)cache->n_streams * keep_stride * 4),
+                          range_of(n_keep, (size_t)cache->n_streams * 4),
+                          range_of(prefix_lens, prefix_lens ? (size_t)cache->n_streams * 4 : 0)};
+  for (const Range& r : small)
+    if (overlap(r, ckv) || overlap(r, kpe)) return DDTREE_ERR_ALIAS;
   ddtree::CompactArgs a{};
   a.ckv = static_cast<uint16_t*>(cache->ckv);
   a.kpe = static_cast<uint16_t*>(cache->kpe);
   a.keep = keep;
   a.n_keep = n_keep;
   a.status = dev_status;
+  a.prefix_lens = prefix_lens;
   a.kv_rows = cache->kv_rows;
   a.n_streams = cache->n_streams;
   a.prefix_len = prefix_len;
   a.keep_stride = keep_stride;
   if (ddtree::launch_compact(a, stream) != hipSuccess) return DDTREE_ERR_HIP;
   return DDTREE_OK;
+}
+
+}  // namespace
+
+int ddtree_compact_kv(const ddtree_kv_cache* cache, int prefix_len, const int32_t* keep,
+                      const int32_t* n_keep, int keep_stride, int32_t* dev_status, hipStream_t stream) {
+  return compact_impl(cache, prefix_len, nullptr, keep, n_keep, keep_stride, dev_status, stream);
+}
+
+int ddtree_compact_kv_ragged(const ddtree_kv_cache* cache, const int32_t* prefix_lens, const int32_t* keep,
+                             const int32_t* n_keep, int keep_stride, int32_t* dev_status, hipStream_t stream) {
+  if (!prefix_lens) return DDTREE_ERR_NULL;
+  return compact_impl(cache, 0, prefix_lens, keep, n_keep, keep_stride, dev_status, stream);
 }
 
 }  // extern "C"
@@ -359,10 +407,12 @@ int ddtree_tree_accept(const int32_t* parents, const int32_t* draft_tokens, cons
   return DDTREE_OK;
 }
 
-int ddtree_accept_compact(const ddtree_kv_cache* cache, int prefix_len, const int32_t* parents,
-                          const int32_t* draft_tokens, const int32_t* target_tokens, int q_len,
-                          int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
-                          int32_t* dev_status, hipStream_t stream) {
+namespace {
+
+int accept_compact_impl(const ddtree_kv_cache* cache, int prefix_len, int32_t* prefix_lens, const int32_t* parents,
+                        const int32_t* draft_tokens, const int32_t* target_tokens, int q_len, int32_t* keep,
+                        int keep_stride, int32_t* n_keep, int32_t* next_token, int32_t* dev_status,
+                        hipStream_t stream) {
   if (!cache || !cache->ckv || !cache->kpe) return DDTREE_ERR_NULL;
   int rc = check_accept(parents, draft_tokens, target_tokens, q_len, cache->n_streams, keep, keep_stride,
                         n_keep, next_token, dev_status);
@@ -370,24 +420,48 @@ int ddtree_accept_compact(const ddtree_kv_cache* cache, int prefix_len, const in
   if (cache->n_streams < 1 || cache->kv_rows < 1 || prefix_len < 0 ||
       (long long)prefix_len + q_len > (long long)cache->kv_rows)
     return DDTREE_ERR_SHAPE;
-  if (!aligned16(cache->ckv) || !aligned16(cache->kpe)) return DDTREE_ERR_ALIGN;
+  if (!aligned16(cache->ckv) || !aligned16(cache->kpe) || (prefix_lens && !aligned4(prefix_lens)))
+    return DDTREE_ERR_ALIGN;
   const Range ckv = range_of(cache->ckv, (size_t)cache->n_streams * cache->kv_rows * kDLat * 2);
   const Range kpe = range_of(cache->kpe, (size_t)cache->n_streams * cache->kv_rows * kDRope * 2);
   if (overlap(ckv, kpe)) return DDTREE_ERR_ALIAS;
   const size_t in_bytes = (size_t)cache->n_streams * q_len * 4;
-  const Range others[6] = {range_of(parents, in_bytes), range_of(draft_tokens, in_bytes),
+  const Range r_pl = range_of(prefix_lens, prefix_lens ? (size_t)cache->n_streams * 4 : 0);
+  const Range others[7] = {range_of(parents, in_bytes), range_of(draft_tokens, in_bytes),
                            range_of(target_tokens, in_bytes),
                            range_of(keep, (size_t)cache->n_streams * keep_stride * 4),
                            range_of(n_keep, (size_t)cache->n_streams * 4),
-                           range_of(next_token, next_token ? (size_t)cache->n_streams * 4 : 0)};
+                           range_of(next_token, next_token ? (size_t)cache->n_streams * 4 : 0), r_pl};
   for (const Range& r : others)
     if (overlap(r, ckv) || overlap(r, kpe)) return DDTREE_ERR_ALIAS;
+  for (int o = 0; o < 6; ++o)
+    if (overlap(others[o], r_pl)) return DDTREE_ERR_ALIAS;
   ddtree::AcceptArgs a = accept_args(parents, draft_tokens, target_tokens, q_len, cache->n_streams, keep,
                                      keep_stride, n_keep, next_token, dev_status);
   a.ckv = static_cast<uint16_t*>(cache->ckv);
   a.kpe = static_cast<uint16_t*>(cache->kpe);
   a.kv_rows = cache->kv_rows;
   a.prefix_len = prefix_len;
+  a.prefix_lens = prefix_lens;
   if (ddtree::launch_accept_compact(a, stream) != hipSuccess) return DDTREE_ERR_HIP;
   return DDTREE_OK;
+}
+
+}  // namespace
+
+int ddtree_accept_compact(const ddtree_kv_cache* cache, int prefix_len, const int32_t* parents,
+                          const int32_t* draft_tokens, const int32_t* target_tokens, int q_len,
+                          int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
+                          int32_t* dev_status, hipStream_t stream) {
+  return accept_compact_impl(cache, prefix_len, nullptr, parents, draft_tokens, target_tokens, q_len, keep,
+                             keep_stride, n_keep, next_token, dev_status, stream);
+}
+
+int ddtree_accept_compact_ragged(const ddtree_kv_cache* cache, int32_t* prefix_lens, const int32_t* parents,
+                                 const int32_t* draft_tokens, const int32_t* target_tokens, int q_len,
+                                 int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
+                                 int32_t* dev_status, hipStream_t stream) {
+  if (!prefix_lens) return DDTREE_ERR_NULL;
+  return accept_compact_impl(cache, 0, prefix_lens, parents, draft_tokens, target_tokens, q_len, keep, keep_stride,
+                             n_keep, next_token, dev_status, stream);
 }

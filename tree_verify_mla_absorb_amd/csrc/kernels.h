@@ -33,12 +33,13 @@ struct VerifyArgs {
   float* part_out[2];  // [splits][rows of the group][512] when that group is split
   float* part_lse[2];  // [splits][rows of the group]
   int32_t* status;
-  int prefix_len;
+  const int32_t* prefix_lens;  // per-stream prefix lengths, or null: prefix_len for every stream
+  int prefix_len;      // the prefix length, or with prefix_lens its upper bound
   int q_len;
   int n_streams;
   int kv_rows;
   int n_pairs;         // q_len / 2
-  int n_tiles;         // ceil((prefix_len + q_len) / kTileKeys)
+  int n_tiles;         // ceil((prefix_len + q_len) / kTileKeys), the longest stream
   int splits[2];
   int tiles_per_split[2];
   int wg_count0;       // workgroups of group 0; group 1 follows
@@ -67,6 +68,7 @@ struct CompactArgs {
   const int32_t* keep;
   const int32_t* n_keep;
   int32_t* status;
+  const int32_t* prefix_lens;  // per-stream prefix lengths, or null: prefix_len
   int kv_rows;
   int n_streams;
   int prefix_len;
@@ -85,6 +87,7 @@ struct AcceptArgs {
   int32_t* status;         // or null
   uint16_t* ckv;           // fused compaction only
   uint16_t* kpe;
+  int32_t* prefix_lens;    // fused, per stream: read, then advanced by n_keep; or null
   int kv_rows;
   int prefix_len;
   int q_len;

@@ -181,7 +181,15 @@ verify_attn_kernel(VerifyArgs a) {
   const int q0 = grp == 0 ? 2 * pair : a.q_len - 1;  // first node of the workgroup
   const int n_nodes = grp == 0 ? 2 : 1;
 
-  const int P = a.prefix_len;
+  // Prefix length of this stream: uniform, or read per stream (bounded by prefix_len; a value
+  // outside [0, prefix_len] is flagged, its stream computed with an empty prefix and poisoned).
+  int P = a.prefix_len;
+  bool bad_prefix = false;
+  if (a.prefix_lens != nullptr) {
+    const int pv = __builtin_amdgcn_readfirstlane(a.prefix_lens[s]);
+    bad_prefix = pv < 0 || pv > a.prefix_len;
+    P = bad_prefix ? 0 : pv;
+  }
   const int Q = a.q_len;
   const int L = P + Q;
   const int qi = q0 + (wave >> 1);
@@ -210,6 +218,7 @@ verify_attn_kernel(VerifyArgs a) {
     }
   }
   if (bad && active && a.status != nullptr && lane == 0) atomicOr(a.status, DDTREE_STATUS_BAD_PARENTS);
+  if (bad_prefix && a.status != nullptr && threadIdx.x == 0) atomicOr(a.status, DDTREE_STATUS_BAD_PREFIX);
 
   // Q^T fragments of this wave's head block: lane holds head `head`, dims 16 ks + 8 g .. +7.
   // The 32 latent k-steps stay in VGPRs for the whole key range; the 4 rotary k-steps are
@@ -287,8 +296,10 @@ verify_attn_kernel(VerifyArgs a) {
   float l_run = 0.f;     // this lane's share of the denominator
   float mx_run = -INFINITY;
   const float cs = a.scale_log2e;
+  // This split's tiles of this stream (a split past a short stream's end is empty: it writes
+  // lse = -inf and a zero output, which the merge weighs by 0).
   const int t_begin = sp * a.tiles_per_split[grp];
-  const int t_end = min(a.n_tiles, t_begin + a.tiles_per_split[grp]);
+  const int t_end = min((L + kTileKeys - 1) / kTileKeys, t_begin + a.tiles_per_split[grp]);
   const int t_mask = max(t_begin, min(t_end, P / kTileKeys));  // first tile holding tree keys
 
   // ---- S^T of a tile held in stage stg: 32 latent + 4 rotary k-steps
@@ -456,11 +467,17 @@ verify_attn_kernel(VerifyArgs a) {
     mx_run = fmaxf(mx_run, mx * cs);
   };
 
-  for (int attempt = 0; attempt < 2; ++attempt) {
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
+  for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[hb][db] = f32x16{};
+    for (int db = 0; db < 4; ++db) o[hb][db] = f32x16{};
+  for (int attempt = 0; attempt < 2 && t_begin < t_end; ++attempt) {
+    if (attempt > 0) {
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[hb][db] = f32x16{};
+    }
     l_run = 0.f;
     mx_run = -INFINITY;
 
@@ -506,8 +523,9 @@ verify_attn_kernel(VerifyArgs a) {
   float* l_sh = reinterpret_cast<float*>(smem + kPOff);  // the P buffers are free after the last barrier
   if (g == 0) l_sh[wave * 32 + c32] = lt;
   const int part_rows = grp == 0 ? a.n_streams * a.n_pairs * 2 * kHeads : a.n_streams * kHeads;
+  const float poison = bad_prefix ? __builtin_nanf("") : 0.f;
   if (active && g == 0) {
-    const float lse_v = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY;
+    const float lse_v = (lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY) + poison;
     if (n_split == 1)
       a.lse[((size_t)s * Q + qi) * kHeads + head] = lse_v;
     else
@@ -518,7 +536,7 @@ verify_attn_kernel(VerifyArgs a) {
   for (int hb = 0; hb < 4; ++hb) {
     if ((hb >> 1) >= n_nodes) continue;
     const float lh = l_sh[hb * 32 + c32];
-    const float inv = lh > 0.f ? 1.0f / lh : 0.f;
+    const float inv = (lh > 0.f ? 1.0f / lh : 0.f) + poison;
     const int h = (hb & 1) * 32 + c32;
     float* dst = n_split == 1 ? a.out + (((size_t)s * Q + q0 + (hb >> 1)) * kHeads + h) * kDLat
                               : a.part_out[grp] + ((size_t)sp * part_rows + part_row(hb >> 1, h)) * kDLat;
