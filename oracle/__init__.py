@@ -9,6 +9,7 @@ Everything is written out from its definition, in float64, with no blocking or f
 * ``verify_attn``   -- masked softmax attention in the absorbed MLA form.
 * ``compact_kv``    -- the out-of-place gather of the kept tree rows into the prefix.
 * ``tree_accept``   -- the greedy walk that picks the accepted path (the rows to keep).
+* ``tree_build``    -- the best-first expansion of the drafter's top-k into the draft tree.
 
 Every function is pinned by the CPU tests (brute force over all small trees, causal attention
 for a chain, per-path causal attention, closed forms, lse merge, equivariances, the absorb
@@ -29,3 +30,4 @@ from .verify import (  # noqa: F401
 )
 from .compact import compact_kv, compact_kv_ragged, validate_keep  # noqa: F401
 from .accept import tree_accept, tree_accept_streams, validate_parents  # noqa: F401
+from .build import tree_build  # noqa: F401

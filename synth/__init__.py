@@ -29,7 +29,7 @@ D_ROPE = 64
 MAX_DEPTH = 15
 
 TAG_Q_LAT, TAG_Q_PE, TAG_CKV, TAG_KPE, TAG_PARENTS, TAG_LEAF = 0, 1, 2, 3, 4, 5
-TAG_DRAFT_TOK, TAG_TARGET_TOK, TAG_ACCEPT_DEPTH = 6, 7, 8
+TAG_DRAFT_TOK, TAG_TARGET_TOK, TAG_ACCEPT_DEPTH, TAG_DRAFTER = 6, 7, 8, 9
 VOCAB = 163840  # synthetic vocabulary size for token ids
 
 
@@ -191,6 +191,23 @@ def make_batch(w: Workload, streams: int | None = None, with_path: bool = True) 
             draft[s] = draft_tokens(rng_for(w.seed, s, TAG_DRAFT_TOK), parents[s])
             target[s] = target_tokens(rng_for(w.seed, s, TAG_TARGET_TOK), parents[s], draft[s], path)
     return Batch(w, q_lat, q_pe, ckv, kpe, parents, keep, n_keep, draft, target)
+
+
+def drafter_topk(seed: int, stream: int, depth: int, topk: int, vocab: int = 1000, temperature: float = 2.0):
+    """A drafter's per-position top-k for one request: ``(lp [depth, topk] float32, tok [depth,
+    topk] int32)``.  Each position's logits are N(0, temperature^2) over ``vocab`` ids; ``lp`` are
+    the log-softmax values of the ``topk`` most likely ids, in decreasing order, and ``tok`` those
+    ids (distinct within a position)."""
+    rng = rng_for(seed, stream, TAG_DRAFTER)
+    lp = np.empty((depth, topk), np.float32)
+    tok = np.empty((depth, topk), np.int32)
+    for d in range(depth):
+        logits = rng.standard_normal(vocab) * temperature
+        logp = logits - (np.log(np.exp(logits - logits.max()).sum()) + logits.max())
+        order = np.argsort(-logp, kind="stable")[:topk]
+        lp[d] = logp[order].astype(np.float32)
+        tok[d] = order.astype(np.int32)
+    return lp, tok
 
 
 def accept_case(seed: int, stream: int, q_len: int, tree: str = "uniform", vocab: int = VOCAB):
