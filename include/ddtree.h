@@ -14,7 +14,14 @@
  *
  *   ddtree_tree_accept   greedy acceptance of the verified tree (sections "The Crash That
  *                        Demanded a Fix" and "What Was Learned");
- *   ddtree_accept_compact  acceptance and compaction in one launch.
+ *   ddtree_accept_compact  acceptance and compaction in one launch;
+ *
+ * and the step before them, described on "Building the Foundation: Architecting a Native CUDA
+ * DDTree Inference Engine":
+ *
+ *   ddtree_tree_build    best-first construction of the draft tree from the drafter's
+ *                        per-position top-k (sections "Tie-Breaking and Numerical Precision"
+ *                        and "The Single-Threaded Heap Design").
  *
  * Conventions shared by every call
  * --------------------------------
@@ -247,6 +254,44 @@ int ddtree_accept_compact_ragged(const ddtree_kv_cache* cache, int32_t* prefix_l
                                  const int32_t* draft_tokens, const int32_t* target_tokens, int q_len,
                                  int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
                                  int32_t* dev_status, hipStream_t stream);
+
+/*
+ * ddtree_tree_build -- best-first draft trees, one launch for all requests (streams).
+ *
+ * For every stream s, with lp = logprobs[s] ([depth][topk], each row in decreasing order) and
+ * tok = topk_tokens[s] ([depth][topk]): node 0 is the root (depth 0, token root_tokens[s] or -1,
+ * log-weight 0).  A heap of candidates starts with the root's first child (depth 1, rank 0,
+ * log-weight lp[0][0]).  Each of up to `budget` steps pops the candidate with the highest
+ * log-weight (equal weights: the earliest inserted), appends it as the next node (token
+ * tok[d-1][r]) and inserts, in this order, its next sibling when r + 1 < topk (log-weight
+ * (logw - lp[d-1][r]) + lp[d-1][r+1], float32, in that order) and its first child when d < depth
+ * (log-weight logw + lp[d][0]).  The heap runs empty early only when topk == 1 and
+ * depth < budget.
+ *
+ * Arguments (device pointers, 4-byte aligned; anc 8-byte aligned; Q = budget + 1):
+ *   logprobs      fp32  [n_streams][depth][topk]
+ *   topk_tokens   int32 [n_streams][depth][topk]
+ *   root_tokens   int32 [n_streams] or NULL
+ *   parents       int32 [n_streams][Q]    written: the tree for ddtree_verify_attn (parents[0] = -1)
+ *   node_tokens   int32 [n_streams][Q]    written: the draft tokens for ddtree_tree_accept
+ *   n_nodes       int32 [n_streams]       written: nodes built (budget + 1 unless the heap ran
+ *                                         empty); entries from n_nodes on are left unchanged
+ *   depths        int32 [n_streams][Q]    or NULL
+ *   logw          fp32  [n_streams][Q]    or NULL
+ *   first_child   int32 [n_streams][Q]    or NULL (-1: none)
+ *   next_sibling  int32 [n_streams][Q]    or NULL (-1: none)
+ *   anc           uint64 [n_streams][Q]   or NULL: bit j of anc[s][i] set iff node j is i or an
+ *                                         ancestor of i (the visibility relation)
+ * Sizes: 1 <= depth <= 64, 1 <= topk <= 64, 1 <= budget <= 63 (a tree of at most 64 nodes, the
+ * verify attention's limit), 1 <= n_streams.
+ * Errors: DDTREE_ERR_NULL / _SHAPE / _ALIGN / _ALIAS (an output overlapping an input or another
+ * output) / _HIP.  Non-finite or unsorted log-probabilities give a well-defined expansion of the
+ * same rule; no input value causes an out-of-bounds access.
+ */
+int ddtree_tree_build(const float* logprobs, const int32_t* topk_tokens, const int32_t* root_tokens, int depth,
+                      int topk, int budget, int n_streams, int32_t* parents, int32_t* node_tokens,
+                      int32_t* n_nodes, int32_t* depths, float* logw, int32_t* first_child,
+                      int32_t* next_sibling, uint64_t* anc, hipStream_t stream);
 
 /* Static text for a return code. */
 const char* ddtree_status_string(int code);

@@ -182,3 +182,19 @@ def test_ragged_argument_errors():
     assert L.ddtree_accept_compact_ragged(ctypes.byref(c), None, A, B, C, 9, D, 9, E, F, None, None) == _lib.ERR_NULL
     assert L.ddtree_accept_compact_ragged(ctypes.byref(c), D + 8, A, B, C, 9, D, 9, E, F, None,
                                           None) == _lib.ERR_ALIAS  # prefix_lens inside keep
+
+
+def build(lp=A, tok=B, d=8, k=4, budget=32, s=2, parents=C, tokens=D, n_nodes=E, anc=None):
+    return _lib.LIB.ddtree_tree_build(lp, tok, None, d, k, budget, s, parents, tokens, n_nodes, None, None, None, None,
+                                      anc, None)
+
+
+def test_build_argument_errors():
+    for field in ("lp", "tok", "parents", "tokens", "n_nodes"):
+        assert build(**{field: None}) == _lib.ERR_NULL
+    for kw in (dict(d=0), dict(d=65), dict(k=0), dict(k=65), dict(budget=0), dict(budget=64), dict(s=0)):
+        assert build(**kw) == _lib.ERR_SHAPE
+    assert build(lp=A + 2) == _lib.ERR_ALIGN
+    assert build(anc=F + 4) == _lib.ERR_ALIGN
+    assert build(parents=A) == _lib.ERR_ALIAS            # output over an input
+    assert build(tokens=C + 4 * 33) == _lib.ERR_ALIAS    # node_tokens inside parents ([2][33] int32)

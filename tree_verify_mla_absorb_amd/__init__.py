@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     num_splits,
     status_string,
     tree_accept,
+    tree_build,
     verify_attn,
     verify_attn_ex,
     verify_attn_ragged,

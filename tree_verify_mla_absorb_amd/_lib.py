@@ -47,6 +47,8 @@ def _load() -> ctypes.CDLL:
     lib.ddtree_compact_kv_ragged.restype = i32
     lib.ddtree_accept_compact_ragged.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp]
     lib.ddtree_accept_compact_ragged.restype = i32
+    lib.ddtree_tree_build.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ddtree_tree_build.restype = i32
     lib.ddtree_status_string.argtypes = [i32]
     lib.ddtree_status_string.restype = ctypes.c_char_p
     lib.ddtree_version.argtypes = []
@@ -67,6 +69,7 @@ EXPORTED = (
     "ddtree_verify_attn_ragged",
     "ddtree_compact_kv_ragged",
     "ddtree_accept_compact_ragged",
+    "ddtree_tree_build",
     "ddtree_status_string",
     "ddtree_version",
 )
@@ -308,3 +311,36 @@ def accept_compact_ragged(ckv, kpe, prefix_lens, parents, draft_tokens, target_t
                                             int(keep.shape[1]), _ptr(n_keep), _ptr(next_token), _ptr(status),
                                             _stream(stream)))
     return keep, n_keep, next_token
+
+
+def tree_build(logprobs, topk_tokens, budget: int, *, root_tokens=None, extras: bool = False, stream=None):
+    """``ddtree_tree_build``: ``logprobs`` fp32 ``[S, D, K]`` (rows decreasing), ``topk_tokens`` int32
+    ``[S, D, K]``.  Returns ``(parents, node_tokens, n_nodes)`` (``[S, budget + 1]`` rows); with
+    ``extras`` also a dict of depths, logw, first_child, next_sibling and anc (int64 view of the
+    uint64 masks)."""
+    _need(logprobs, "logprobs", (torch.float32,))
+    _need(topk_tokens, "topk_tokens", (torch.int32,))
+    if logprobs.dim() != 3 or topk_tokens.shape != logprobs.shape:
+        raise ValueError("logprobs / topk_tokens must share one [S, D, K] shape")
+    if root_tokens is not None:
+        _need(root_tokens, "root_tokens", (torch.int32,))
+    s, d, k = logprobs.shape
+    q = int(budget) + 1
+    dev = logprobs.device
+    parents = torch.full((s, q), -2, dtype=torch.int32, device=dev)
+    tokens = torch.full((s, q), -2, dtype=torch.int32, device=dev)
+    n_nodes = torch.empty((s,), dtype=torch.int32, device=dev)
+    ex = {}
+    if extras:
+        ex = {"depths": torch.full((s, q), -2, dtype=torch.int32, device=dev),
+              "logw": torch.full((s, q), float("nan"), dtype=torch.float32, device=dev),
+              "first_child": torch.full((s, q), -2, dtype=torch.int32, device=dev),
+              "next_sibling": torch.full((s, q), -2, dtype=torch.int32, device=dev),
+              "anc": torch.zeros((s, q), dtype=torch.int64, device=dev)}
+    _check(LIB.ddtree_tree_build(_ptr(logprobs), _ptr(topk_tokens), _ptr(root_tokens), int(d), int(k), int(budget),
+                                 int(s), _ptr(parents), _ptr(tokens), _ptr(n_nodes), _ptr(ex.get("depths")),
+                                 _ptr(ex.get("logw")), _ptr(ex.get("first_child")), _ptr(ex.get("next_sibling")),
+                                 _ptr(ex.get("anc")), _stream(stream)))
+    if extras:
+        return parents, tokens, n_nodes, ex
+    return parents, tokens, n_nodes

@@ -465,3 +465,49 @@ int ddtree_accept_compact_ragged(const ddtree_kv_cache* cache, int32_t* prefix_l
   return accept_compact_impl(cache, 0, prefix_lens, parents, draft_tokens, target_tokens, q_len, keep, keep_stride,
                              n_keep, next_token, dev_status, stream);
 }
+
+int ddtree_tree_build(const float* logprobs, const int32_t* topk_tokens, const int32_t* root_tokens, int depth,
+                      int topk, int budget, int n_streams, int32_t* parents, int32_t* node_tokens,
+                      int32_t* n_nodes, int32_t* depths, float* logw, int32_t* first_child,
+                      int32_t* next_sibling, uint64_t* anc, hipStream_t stream) {
+  if (!logprobs || !topk_tokens || !parents || !node_tokens || !n_nodes) return DDTREE_ERR_NULL;
+  if (depth < 1 || depth > 64 || topk < 1 || topk > 64 || budget < 1 || budget > kMaxQ - 1 || n_streams < 1)
+    return DDTREE_ERR_SHAPE;
+  if (!aligned4(logprobs) || !aligned4(topk_tokens) || (root_tokens && !aligned4(root_tokens)) ||
+      !aligned4(parents) || !aligned4(node_tokens) || !aligned4(n_nodes) || (depths && !aligned4(depths)) ||
+      (logw && !aligned4(logw)) || (first_child && !aligned4(first_child)) ||
+      (next_sibling && !aligned4(next_sibling)) || (anc && (reinterpret_cast<uintptr_t>(anc) & 7u)))
+    return DDTREE_ERR_ALIGN;
+  const size_t q = (size_t)budget + 1, S = (size_t)n_streams;
+  const size_t in_bytes = S * depth * topk * 4;
+  const Range ins[3] = {range_of(logprobs, in_bytes), range_of(topk_tokens, in_bytes),
+                        range_of(root_tokens, root_tokens ? S * 4 : 0)};
+  const Range outs[8] = {range_of(parents, S * q * 4), range_of(node_tokens, S * q * 4), range_of(n_nodes, S * 4),
+                         range_of(depths, depths ? S * q * 4 : 0), range_of(logw, logw ? S * q * 4 : 0),
+                         range_of(first_child, first_child ? S * q * 4 : 0),
+                         range_of(next_sibling, next_sibling ? S * q * 4 : 0), range_of(anc, anc ? S * q * 8 : 0)};
+  for (int o = 0; o < 8; ++o) {
+    for (const Range& r : ins)
+      if (overlap(outs[o], r)) return DDTREE_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 8; ++o2)
+      if (overlap(outs[o], outs[o2])) return DDTREE_ERR_ALIAS;
+  }
+  ddtree::BuildArgs a{};
+  a.lp = logprobs;
+  a.tok = topk_tokens;
+  a.root_tok = root_tokens;
+  a.parents = parents;
+  a.tokens = node_tokens;
+  a.n_nodes = n_nodes;
+  a.depths = depths;
+  a.logw = logw;
+  a.first_child = first_child;
+  a.next_sibling = next_sibling;
+  a.anc = reinterpret_cast<unsigned long long*>(anc);
+  a.depth = depth;
+  a.topk = topk;
+  a.budget = budget;
+  a.n_streams = n_streams;
+  if (ddtree::launch_build(a, stream) != hipSuccess) return DDTREE_ERR_HIP;
+  return DDTREE_OK;
+}

@@ -96,6 +96,26 @@ struct AcceptArgs {
 };
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+
+struct BuildArgs {
+  const float* lp;            // [n_streams][depth][topk], decreasing within a position
+  const int32_t* tok;         // [n_streams][depth][topk]
+  const int32_t* root_tok;    // [n_streams] or null
+  int32_t* parents;           // [n_streams][budget + 1]
+  int32_t* tokens;            // [n_streams][budget + 1]
+  int32_t* n_nodes;           // [n_streams]
+  int32_t* depths;            // [n_streams][budget + 1] or null
+  float* logw;                // [n_streams][budget + 1] or null
+  int32_t* first_child;       // [n_streams][budget + 1] or null
+  int32_t* next_sibling;      // [n_streams][budget + 1] or null
+  unsigned long long* anc;    // [n_streams][budget + 1] or null
+  int depth;                  // 1..64
+  int topk;                   // 1..64
+  int budget;                 // 1..63
+  int n_streams;
+};
+
+hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_accept_compact(const AcceptArgs& a, hipStream_t stream);
 
 }  // namespace ddtree
