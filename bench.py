@@ -9,7 +9,8 @@ token ids (no dataset is involved) and are resident in HBM before the timed regi
 Prints one JSON line.  ``value`` is TFLOP/s of the verify attention counted over visible
 (query, key) pairs only, divided by the whole step time (verify + accept + compaction).  The
 ``detail`` object also carries per-call times of ``ddtree_tree_accept`` over the stream and
-budget grid the pages report, of the fused call, and of ``ddtree_compact_kv`` alone.
+budget grid the pages report, of the fused call, of ``ddtree_compact_kv`` alone, and of
+``ddtree_tree_build`` (depth 15, top-8) for 1/8/64 requests and budgets 8/32/63.
 """
 from __future__ import annotations
 
@@ -136,6 +137,31 @@ def accept_table(lib, dev):
             nxt = torch.empty((streams,), dtype=torch.int32, device=dev)
             us = time_calls(lambda: lib.tree_accept(par, dr, tg, keep=keep, n_keep=n_keep, next_token=nxt))
             table[f"streams{streams}_budget{q - 1}"] = round(us, 2)
+    return table
+
+
+def build_table(lib, dev, depth: int = 15, topk: int = 8):
+    """``ddtree_tree_build`` us/call for 1, 8, 64 requests and budgets 8, 32, 63 (depth 15, top-8)."""
+    import torch
+    import synth
+    table = {}
+    for streams in (1, 8, 64):
+        pairs = [synth.drafter_topk(60, s, depth, topk) for s in range(streams)]
+        lp = torch.from_numpy(np.stack([p[0] for p in pairs])).to(dev)
+        tok = torch.from_numpy(np.stack([p[1] for p in pairs])).to(dev)
+        for budget in (8, 32, 63):
+            par = torch.empty((streams, budget + 1), dtype=torch.int32, device=dev)
+            ntok = torch.empty_like(par)
+            n = torch.empty((streams,), dtype=torch.int32, device=dev)
+            args = [lib._ptr(lp), lib._ptr(tok), None, depth, topk, budget, streams, lib._ptr(par), lib._ptr(ntok),
+                    lib._ptr(n), None, None, None, None, None]
+
+            def call():
+                rc = lib.LIB.ddtree_tree_build(*args, lib._stream(None))
+                assert rc == 0, rc
+
+            us = time_calls(call)
+            table[f"streams{streams}_budget{budget}"] = round(us, 2)
     return table
 
 
@@ -295,6 +321,7 @@ def main() -> int:
 
     # per-call times of the acceptance and compaction entry points (outside the timed steps)
     accept_us = accept_table(_lib, dev)
+    build_us = build_table(_lib, dev)
     fused_us = time_calls(lambda: _lib.accept_compact(ckv, kpe, w.prefix, parents, draft_tok, target_tok, keep=keep,
                                                       n_keep=n_keep, next_token=next_tok))
     compact_us = time_calls(lambda: _lib.compact_kv(ckv, kpe, w.prefix, keep, n_keep))
@@ -326,6 +353,7 @@ def main() -> int:
                    "accept_compact_us_per_call": round(fused_us, 2),
                    "compact_kv_us_per_call": round(compact_us, 2),
                    "tree_accept_us_per_call": accept_us,
+                   "tree_build_us_per_call": build_us,
                    "verify_tflops": round(achieved, 2),
                    "pct_mfma_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
                    "algorithmic_bytes": algorithmic_bytes(w, w.streams),

@@ -14,7 +14,7 @@
 // of order-preserving keys of the log-weights, and two ballots pick the earliest-inserted
 // candidate among equal weights -- exactly the heap's order.  Node i's outputs live in lane i
 // and are filled as the node is appended: its ancestor mask is its parent's (read across lanes)
-// plus its own bit, and the retrieve links chain each parent's children in append order.
+// plus its own bit.  The retrieve links come from the parents in one pass at the end.
 // The drafter's log-probabilities and tokens of the request are staged in LDS once.
 
 #include "kernels.h"
@@ -62,83 +62,90 @@ __global__ void __launch_bounds__(64) tree_build_kernel(BuildArgs a) {
   }
   __syncthreads();
 
-  // candidate slots (slot c: lane c % 64, sub-slot c / 64)
-  bool live[2] = {false, false};
-  float cw[2] = {0.f, 0.f};
-  int cd[2] = {0, 0}, cr[2] = {0, 0}, cp[2] = {0, 0};
+  // Candidate slots (slot c: lane c % 64, sub-slot c / 64), one register per field and
+  // sub-slot: a candidate's weight, depth, rank and parent.  Updates are per-lane selects, not
+  // branches, so a pop costs a few dozen wave instructions.
+  float w0 = 0.f, w1 = 0.f;
+  int d0 = 0, d1 = 0, r0 = 0, r1 = 0, p0 = 0, p1 = 0;
+  bool l0 = lane == 0, l1 = false;  // live; slot 0 = the root's first child
+  if (lane == 0) {
+    w0 = lp_s[0];
+    d0 = 1;
+  }
   // node `lane`
-  int my_parent = -1, my_depth = 0, my_rank = 0, my_tok = -1, my_fc = -1, my_ns = -1, my_last = -1;
+  int my_parent = -1, my_depth = 0, my_rank = 0, my_tok = lane == 0 && a.root_tok != nullptr ? a.root_tok[s] : -1;
   float my_w = 0.f;
   unsigned long long my_anc = lane == 0 ? 1ull : 0ull;
-  if (lane == 0) {
-    my_tok = a.root_tok != nullptr ? a.root_tok[s] : -1;
-    live[0] = true;
-    cw[0] = lp_s[0];
-    cd[0] = 1;
-  }
   int n = 1, n_ins = 1;
   for (int step = 0; step < B; ++step) {
-    const unsigned k0 = live[0] ? ordered_key(cw[0]) : 0u;
-    const unsigned k1 = live[1] ? ordered_key(cw[1]) : 0u;
+    const unsigned k0 = l0 ? ordered_key(w0) : 0u;
+    const unsigned k1 = l1 ? ordered_key(w1) : 0u;
     const unsigned m = wave_max_u32(max(k0, k1));
     if (m == 0) break;  // no candidate left (top-1 chain shorter than the budget)
     const unsigned long long b0 = __builtin_amdgcn_ballot_w64(k0 == m);
     const unsigned long long b1 = __builtin_amdgcn_ballot_w64(k1 == m);
-    const int ins = b0 != 0 ? (int)__builtin_ctzll(b0) : 64 + (int)__builtin_ctzll(b1);
-    const int owner = ins & 63, sub = ins >> 6;
-    const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(sub ? cw[1] : cw[0]), owner));
-    const int d = __builtin_amdgcn_readlane(sub ? cd[1] : cd[0], owner);
-    const int r = __builtin_amdgcn_readlane(sub ? cr[1] : cr[0], owner);
-    const int p = __builtin_amdgcn_readlane(sub ? cp[1] : cp[0], owner);
-    if (lane == owner) live[sub] = false;
+    int d, r, p;
+    float w;
+    if (b0 != 0) {  // uniform: the earliest-inserted maximum sits in sub-slot 0 of lane `owner`
+      const int owner = (int)__builtin_ctzll(b0);
+      w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(w0), owner));
+      d = __builtin_amdgcn_readlane(d0, owner);
+      r = __builtin_amdgcn_readlane(r0, owner);
+      p = __builtin_amdgcn_readlane(p0, owner);
+      l0 = l0 && lane != owner;
+    } else {
+      const int owner = (int)__builtin_ctzll(b1);
+      w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(w1), owner));
+      d = __builtin_amdgcn_readlane(d1, owner);
+      r = __builtin_amdgcn_readlane(r1, owner);
+      p = __builtin_amdgcn_readlane(p1, owner);
+      l1 = l1 && lane != owner;
+    }
     const int idx = n++;
-    // append node idx
-    // the parent's mask, read across lanes as two 32-bit halves (zero-extended: bit 31 of the
-    // low half is a node, not a sign)
+    // append node idx: the parent's mask, read across lanes as two 32-bit halves
+    // (zero-extended: bit 31 of the low half is a node, not a sign)
     const unsigned long long pa =
         (unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(unsigned)(my_anc & 0xffffffffu), p) |
         ((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(unsigned)(my_anc >> 32), p) << 32);
-    const int prev = __builtin_amdgcn_readlane(my_last, p);
-    if (lane == idx) {
-      my_parent = p;
-      my_depth = d;
-      my_rank = r;
-      my_tok = tok_s[(d - 1) * K + r];
-      my_w = w;
-      my_anc = pa | (1ull << idx);
-    }
-    if (prev >= 0) {
-      if (lane == prev) my_ns = idx;
-    } else if (lane == p) {
-      my_fc = idx;
-    }
-    if (lane == p) my_last = idx;
+    const int t = tok_s[(d - 1) * K + r];
+    const bool me = lane == idx;
+    my_parent = me ? p : my_parent;
+    my_depth = me ? d : my_depth;
+    my_rank = me ? r : my_rank;
+    my_tok = me ? t : my_tok;
+    my_w = me ? w : my_w;
+    my_anc = me ? (pa | (1ull << idx)) : my_anc;
     if (step + 1 == B) break;  // no further pops: nothing to offer
-    // offer the next sibling, then the first child
-    if (r + 1 < K) {
-      const float ws = (w - lp_s[(d - 1) * K + r]) + lp_s[(d - 1) * K + r + 1];
-      if (lane == (n_ins & 63)) {
-        const int c = n_ins >> 6;
-        live[c] = true;
-        cw[c] = ws;
-        cd[c] = d;
-        cr[c] = r + 1;
-        cp[c] = p;
-      }
-      ++n_ins;
-    }
-    if (d < D) {
-      const float wc = w + lp_s[d * K];
-      if (lane == (n_ins & 63)) {
-        const int c = n_ins >> 6;
-        live[c] = true;
-        cw[c] = wc;
-        cd[c] = d + 1;
-        cr[c] = 0;
-        cp[c] = idx;
-      }
-      ++n_ins;
-    }
+    // offer the next sibling (the pages' float32 expression, in this order), then the first child
+    const bool has_sib = r + 1 < K, has_child = d < D;
+    const float ws = has_sib ? (w - lp_s[(d - 1) * K + r]) + lp_s[(d - 1) * K + r + 1] : 0.f;
+    const float wc = has_child ? w + lp_s[d * K] : 0.f;
+    const int slot_s = n_ins, slot_c = n_ins + (has_sib ? 1 : 0);
+    n_ins = slot_c + (has_child ? 1 : 0);
+    // per lane: does this lane own the sibling's / the child's slot, in sub-slot 0 or 1?
+    const bool own_s = has_sib && lane == (slot_s & 63), own_c = has_child && lane == (slot_c & 63);
+    const bool s_in0 = own_s && slot_s < 64, s_in1 = own_s && slot_s >= 64;
+    const bool c_in0 = own_c && slot_c < 64, c_in1 = own_c && slot_c >= 64;
+    w0 = s_in0 ? ws : (c_in0 ? wc : w0);
+    d0 = s_in0 ? d : (c_in0 ? d + 1 : d0);
+    r0 = s_in0 ? r + 1 : (c_in0 ? 0 : r0);
+    p0 = s_in0 ? p : (c_in0 ? idx : p0);
+    l0 = l0 || s_in0 || c_in0;
+    w1 = s_in1 ? ws : (c_in1 ? wc : w1);
+    d1 = s_in1 ? d : (c_in1 ? d + 1 : d1);
+    r1 = s_in1 ? r + 1 : (c_in1 ? 0 : r1);
+    p1 = s_in1 ? p : (c_in1 ? idx : p1);
+    l1 = l1 || s_in1 || c_in1;
+  }
+  // Retrieve links, from the parents: children of a node were appended in rank order, so the
+  // first child is the lowest index with that parent and the next sibling the next such index.
+  int my_fc = -1, my_ns = -1;
+  for (int j = 0; j < n; ++j) {
+    const int pj = __builtin_amdgcn_readlane(my_parent, j);
+    const unsigned long long kids = __builtin_amdgcn_ballot_w64(lane < n && my_parent == j);
+    if (lane == j) my_fc = kids != 0 ? (int)__builtin_ctzll(kids) : -1;
+    const unsigned long long sibs = __builtin_amdgcn_ballot_w64(lane < n && lane > j && my_parent == pj);
+    if (lane == j && j > 0) my_ns = sibs != 0 ? (int)__builtin_ctzll(sibs) : -1;
   }
   const size_t row = (size_t)s * (B + 1) + lane;
   if (lane < n) {
