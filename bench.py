@@ -165,6 +165,36 @@ def build_table(lib, dev, depth: int = 15, topk: int = 8):
     return table
 
 
+def layers_table(lib, dev, w, parents, draft_tok, target_tok, keep_bits, n_keep_bits, n_layers: int = 61):
+    """Acceptance plus compaction of ``n_layers`` caches of the workload's geometry (61: the
+    DeepSeek-V3 / Kimi-K2 layer count): one ``ddtree_accept_compact_layers`` call against one
+    ``ddtree_accept_compact`` call per layer.  The caches are device allocations whose contents do
+    not matter (the gather copies bits)."""
+    import torch
+    rows = w.kv_rows
+    caches = [(torch.empty((w.streams, rows, 512), dtype=torch.bfloat16, device=dev),
+               torch.empty((w.streams, rows, 64), dtype=torch.bfloat16, device=dev)) for _ in range(n_layers)]
+    keep = torch.empty((w.streams, w.q_len), dtype=torch.int32, device=dev)
+    n_keep = torch.empty((w.streams,), dtype=torch.int32, device=dev)
+    nxt = torch.empty((w.streams,), dtype=torch.int32, device=dev)
+    fused = time_calls(lambda: lib.accept_compact_layers(caches, w.prefix, parents, draft_tok, target_tok, keep=keep,
+                                                         n_keep=n_keep, next_token=nxt))
+
+    def per_layer():
+        for c, k in caches:
+            lib.accept_compact(c, k, w.prefix, parents, draft_tok, target_tok, keep=keep, n_keep=n_keep,
+                               next_token=nxt)
+
+    looped = time_calls(per_layer, n=20)
+    moved_rows = sum(int((keep_bits[s, :n_keep_bits[s]] != np.arange(n_keep_bits[s])).sum())
+                     for s in range(w.streams))
+    moved_bytes = 2 * moved_rows * (512 + 64) * 2 * n_layers  # read + write of each moved row
+    del caches
+    torch.cuda.empty_cache()
+    return {"layers": n_layers, "us_per_call": round(fused, 2), "per_layer_calls_us": round(looped, 2),
+            "moved_bytes": moved_bytes, "gbs": round(moved_bytes / (fused * 1e-6) / 1e9, 1)}
+
+
 def _db_rows(path: str, sql: str):
     import sqlite3
     con = sqlite3.connect(path)
@@ -325,6 +355,7 @@ def main() -> int:
     fused_us = time_calls(lambda: _lib.accept_compact(ckv, kpe, w.prefix, parents, draft_tok, target_tok, keep=keep,
                                                       n_keep=n_keep, next_token=next_tok))
     compact_us = time_calls(lambda: _lib.compact_kv(ckv, kpe, w.prefix, keep, n_keep))
+    layers = layers_table(_lib, dev, w, parents, draft_tok, target_tok, b.keep, b.n_keep)
 
     flops = 2.0 * w.heads * (576 + 512) * visible_pairs(b.parents, w.prefix)
     tflops_step = flops / (ms_step * 1e-3) / 1e12
@@ -354,6 +385,7 @@ def main() -> int:
                    "compact_kv_us_per_call": round(compact_us, 2),
                    "tree_accept_us_per_call": accept_us,
                    "tree_build_us_per_call": build_us,
+                   "accept_compact_layers": layers,
                    "verify_tflops": round(achieved, 2),
                    "pct_mfma_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
                    "algorithmic_bytes": algorithmic_bytes(w, w.streams),

@@ -15,6 +15,8 @@
  *   ddtree_tree_accept   greedy acceptance of the verified tree (sections "The Crash That
  *                        Demanded a Fix" and "What Was Learned");
  *   ddtree_accept_compact  acceptance and compaction in one launch;
+ *   ddtree_compact_kv_layers, ddtree_accept_compact_layers
+ *                        the same for every layer's cache of a model, in one launch;
  *
  * and the step before them, described on "Building the Foundation: Architecting a Native CUDA
  * DDTree Inference Engine":
@@ -253,6 +255,45 @@ int ddtree_compact_kv_ragged(const ddtree_kv_cache* cache, const int32_t* prefix
 int ddtree_accept_compact_ragged(const ddtree_kv_cache* cache, int32_t* prefix_lens, const int32_t* parents,
                                  const int32_t* draft_tokens, const int32_t* target_tokens, int q_len,
                                  int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
+                                 int32_t* dev_status, hipStream_t stream);
+
+/*
+ * Multi-layer compaction.  A model keeps one latent cache per layer, and the accepted path moves
+ * the same rows in every one of them ("Race Conditions, Buffer Aliasing, and the Architecture of
+ * a Native DDTree Inference Engine": section "The Cache Compaction Problem" for the gather, and
+ * the closing section, which defers fusing it).  These calls compact all layers in one launch.
+ *
+ *   caches      HOST array [n_layers] of cache descriptors; every entry has the same kv_rows
+ *               and n_streams, and no two caches overlap.  Read during the call only.
+ *   n_layers    1 .. DDTREE_MAX_LAYERS
+ *   prefix_len  the prefix of every stream when prefix_lens is NULL (ignored otherwise)
+ *   prefix_lens NULL, or device int32 [n_streams]: per-stream prefixes
+ * For each layer the result is bit-identical to the single-cache call on that layer with the
+ * same arguments.  Each layer's gather is race-free on its own (all reads of a stream's kept
+ * rows precede its writes); layers never share memory.
+ */
+#define DDTREE_MAX_LAYERS 128
+
+/*
+ * ddtree_compact_kv_layers -- ddtree_compact_kv (prefix_lens NULL) or ddtree_compact_kv_ragged
+ * (prefix_lens given, read only) applied to every layer.  A stream whose keep / n_keep or prefix
+ * is invalid is skipped in every layer and flagged once (DDTREE_STATUS_BAD_KEEP / _BAD_PREFIX).
+ */
+int ddtree_compact_kv_layers(const ddtree_kv_cache* caches, int n_layers, int prefix_len, const int32_t* prefix_lens,
+                             const int32_t* keep, const int32_t* n_keep, int keep_stride, int32_t* dev_status,
+                             hipStream_t stream);
+
+/*
+ * ddtree_accept_compact_layers -- acceptance (as ddtree_tree_accept: keep, n_keep, next_token
+ * written once) and the compaction of every layer, one step.  With prefix_lens NULL it matches
+ * ddtree_accept_compact on each layer; with prefix_lens it matches ddtree_accept_compact_ragged,
+ * including the advance prefix_lens[s] += n_keep[s] for every stream whose rows moved (done by a
+ * second, small launch on the same stream, after every layer has read the old value).
+ * Requires prefix_len + q_len <= kv_rows (prefix_lens NULL) or q_len <= kv_rows.
+ */
+int ddtree_accept_compact_layers(const ddtree_kv_cache* caches, int n_layers, int prefix_len, int32_t* prefix_lens,
+                                 const int32_t* parents, const int32_t* draft_tokens, const int32_t* target_tokens,
+                                 int q_len, int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
                                  int32_t* dev_status, hipStream_t stream);
 
 /*

@@ -15,7 +15,8 @@ tree builder on "Building the Foundation: Architecting a Native CUDA DDTree Infe
 section "The Single-Threaded Heap Design" (budget at most 64, depth at most 15).
 
 Every random draw uses ``numpy.random.Generator(PCG64(SeedSequence([seed, stream, tag])))`` so that
-any stream can be regenerated on its own.
+any stream can be regenerated on its own (per-layer caches add the layer:
+``SeedSequence([seed, stream, tag, layer])``).
 """
 from __future__ import annotations
 
@@ -30,6 +31,7 @@ MAX_DEPTH = 15
 
 TAG_Q_LAT, TAG_Q_PE, TAG_CKV, TAG_KPE, TAG_PARENTS, TAG_LEAF = 0, 1, 2, 3, 4, 5
 TAG_DRAFT_TOK, TAG_TARGET_TOK, TAG_ACCEPT_DEPTH, TAG_DRAFTER = 6, 7, 8, 9
+TAG_LAYER_CKV, TAG_LAYER_KPE = 10, 11
 VOCAB = 163840  # synthetic vocabulary size for token ids
 
 
@@ -227,3 +229,18 @@ def random_inputs(seed: int, streams: int, prefix: int, q_len: int, heads: int =
     """Ad-hoc sizes for tests (same recipe as the named workloads)."""
     return make_batch(Workload(f"adhoc-{seed}", streams, prefix, q_len, tree, seed, heads))
 
+
+def layer_caches(seed: int, n_layers: int, streams: int, rows: int):
+    """One latent cache per model layer, all of the same geometry: a list of ``(ckv [streams,
+    rows, 512], kpe [streams, rows, 64])`` bf16 bit arrays, each layer drawn independently."""
+    out = []
+    for layer in range(n_layers):
+        ckv = np.empty((streams, rows, D_LATENT), np.uint16)
+        kpe = np.empty((streams, rows, D_ROPE), np.uint16)
+        for s in range(streams):
+            ckv[s] = bf16_normal(np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+                [seed, s, TAG_LAYER_CKV, layer]))), (rows, D_LATENT))
+            kpe[s] = bf16_normal(np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+                [seed, s, TAG_LAYER_KPE, layer]))), (rows, D_ROPE))
+        out.append((ckv, kpe))
+    return out

@@ -198,3 +198,51 @@ def test_build_argument_errors():
     assert build(anc=F + 4) == _lib.ERR_ALIGN
     assert build(parents=A) == _lib.ERR_ALIAS            # output over an input
     assert build(tokens=C + 4 * 33) == _lib.ERR_ALIAS    # node_tokens inside parents ([2][33] int32)
+
+
+def layer_table(n, rows=300, s=2, bad=None):
+    """n fake caches, far apart above 4 GiB; ``bad`` = (layer, field, value) overrides one entry."""
+    t = (_lib.KVCache * max(n, 1))()
+    for i in range(n):
+        t[i] = _lib.KVCache(0x100000000 + i * 0x200000, 0x100000000 + i * 0x200000 + 0x100000, rows, s)
+    if bad is not None:
+        setattr(t[bad[0]], bad[1], bad[2])
+    return t
+
+
+def compact_layers(n=4, prefix=100, prefix_lens=None, keep=E, n_keep=F, stride=33, table=None):
+    t = layer_table(n) if table is None else table
+    return _lib.LIB.ddtree_compact_kv_layers(t, n, prefix, prefix_lens, keep, n_keep, stride, None, None)
+
+
+def accept_layers(n=4, prefix=100, prefix_lens=None, q=9, keep=D, parents=A, table=None):
+    t = layer_table(n) if table is None else table
+    return _lib.LIB.ddtree_accept_compact_layers(t, n, prefix, prefix_lens, parents, B, C, q, keep, q, E, F, None,
+                                                 None)
+
+
+@pytest.mark.parametrize("call", [compact_layers, accept_layers])
+def test_layers_argument_errors(call):
+    assert call(table=None, n=0) == _lib.ERR_SHAPE
+    assert call(n=_lib.MAX_LAYERS + 1) == _lib.ERR_SHAPE
+    assert call(table=layer_table(4, bad=(2, "ckv", None))) == _lib.ERR_NULL
+    assert call(table=layer_table(4, bad=(3, "kv_rows", 301))) == _lib.ERR_SHAPE     # geometry differs
+    assert call(table=layer_table(4, bad=(1, "n_streams", 3))) == _lib.ERR_SHAPE
+    assert call(table=layer_table(4, bad=(2, "kpe", 0x100000000 + 2 * 0x200000 + 8))) == _lib.ERR_ALIGN
+    # layer 3's latent cache starts inside layer 2's
+    assert call(table=layer_table(4, bad=(3, "ckv", 0x100000000 + 2 * 0x200000 + 0x1000))) == _lib.ERR_ALIAS
+    # the last of 128 layers is checked too
+    t = layer_table(_lib.MAX_LAYERS, bad=(_lib.MAX_LAYERS - 1, "kpe", 0x100000000 + 5 * 0x200000))
+    assert call(n=_lib.MAX_LAYERS, table=t) == _lib.ERR_ALIAS
+    assert call(keep=0x100000000 + 3 * 0x200000 + 0x100040) == _lib.ERR_ALIAS       # keep inside layer 3's kpe
+    assert call(prefix=-1) == _lib.ERR_SHAPE
+    assert call(prefix_lens=G + 2) == _lib.ERR_ALIGN
+
+
+def test_layers_prefix_bounds():
+    assert compact_layers(prefix=301) == _lib.ERR_SHAPE          # prefix past the cache rows
+    assert accept_layers(prefix=292) == _lib.ERR_SHAPE           # tree block past the cache rows
+    assert accept_layers(prefix=-5, prefix_lens=G, q=0) == _lib.ERR_SHAPE
+    assert accept_layers(prefix_lens=D + 8) == _lib.ERR_ALIAS    # prefix_lens inside keep
+    assert compact_layers(keep=None) == _lib.ERR_NULL
+    assert accept_layers(parents=None) == _lib.ERR_NULL

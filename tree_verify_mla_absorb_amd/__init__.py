@@ -8,8 +8,10 @@ The compute lives in ``libddtree.so`` (C ABI, ``include/ddtree.h``); this packag
 from ._lib import (  # noqa: F401
     DDTreeError,
     accept_compact,
+    accept_compact_layers,
     accept_compact_ragged,
     compact_kv,
+    compact_kv_layers,
     compact_kv_ragged,
     num_splits,
     status_string,

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libddtree.so")
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = -1, -2, -3, -4, -5, -6
 STATUS_BAD_PARENTS, STATUS_BAD_KEEP, STATUS_BAD_PREFIX = 1, 2, 4
-HEADS, D_LATENT, D_ROPE, MAX_Q_LEN = 64, 512, 64, 64
+HEADS, D_LATENT, D_ROPE, MAX_Q_LEN, MAX_LAYERS = 64, 512, 64, 64, 128
 
 
 def _load() -> ctypes.CDLL:
@@ -49,6 +49,10 @@ def _load() -> ctypes.CDLL:
     lib.ddtree_accept_compact_ragged.restype = i32
     lib.ddtree_tree_build.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ddtree_tree_build.restype = i32
+    lib.ddtree_compact_kv_layers.argtypes = [vp, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.ddtree_compact_kv_layers.restype = i32
+    lib.ddtree_accept_compact_layers.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp]
+    lib.ddtree_accept_compact_layers.restype = i32
     lib.ddtree_status_string.argtypes = [i32]
     lib.ddtree_status_string.restype = ctypes.c_char_p
     lib.ddtree_version.argtypes = []
@@ -70,6 +74,8 @@ EXPORTED = (
     "ddtree_compact_kv_ragged",
     "ddtree_accept_compact_ragged",
     "ddtree_tree_build",
+    "ddtree_compact_kv_layers",
+    "ddtree_accept_compact_layers",
     "ddtree_status_string",
     "ddtree_version",
 )
@@ -310,6 +316,64 @@ def accept_compact_ragged(ckv, kpe, prefix_lens, parents, draft_tokens, target_t
                                             _ptr(draft_tokens), _ptr(target_tokens), int(q), _ptr(keep),
                                             int(keep.shape[1]), _ptr(n_keep), _ptr(next_token), _ptr(status),
                                             _stream(stream)))
+    return keep, n_keep, next_token
+
+
+def _layer_table(caches):
+    """``caches``: a sequence of ``(ckv [S, rows, 512], kpe [S, rows, 64])`` pairs, one per layer."""
+    caches = list(caches)
+    if not caches:
+        raise ValueError("at least one layer")
+    table = (KVCache * len(caches))()
+    for i, (ckv, kpe) in enumerate(caches):
+        _need(ckv, f"caches[{i}].ckv", _BF16)
+        _need(kpe, f"caches[{i}].kpe", _BF16)
+        if kpe.shape[:2] != ckv.shape[:2]:
+            raise ValueError("shape mismatch")
+        table[i] = KVCache(ckv.data_ptr(), kpe.data_ptr(), int(ckv.shape[1]), int(ckv.shape[0]))
+    return table, int(caches[0][0].shape[0])
+
+
+def _prefix_arg(prefix, s):
+    """An int (every stream) or a device int32 ``[S]`` tensor (per stream)."""
+    if isinstance(prefix, torch.Tensor):
+        _need(prefix, "prefix_lens", (torch.int32,))
+        if prefix.shape != (s,):
+            raise ValueError("prefix_lens must be [S]")
+        return 0, _ptr(prefix)
+    return int(prefix), None
+
+
+def compact_kv_layers(caches, prefix, keep, n_keep, *, status=None, stream=None) -> None:
+    """``ddtree_compact_kv_layers``: the compaction of ``compact_kv`` (``prefix`` an int) or
+    ``compact_kv_ragged`` (``prefix`` a device int32 ``[S]``, read only) applied to every layer's
+    ``(ckv, kpe)`` in ``caches``, in one launch."""
+    table, s = _layer_table(caches)
+    _need(keep, "keep", (torch.int32,))
+    _need(n_keep, "n_keep", (torch.int32,))
+    if status is not None:
+        _need(status, "status", (torch.int32,))
+    if keep.dim() != 2 or keep.shape[0] != s or n_keep.shape != (s,):
+        raise ValueError("shape mismatch")
+    p, pl = _prefix_arg(prefix, s)
+    _check(LIB.ddtree_compact_kv_layers(table, len(table), p, pl, _ptr(keep), _ptr(n_keep), int(keep.shape[1]),
+                                        _ptr(status), _stream(stream)))
+
+
+def accept_compact_layers(caches, prefix, parents, draft_tokens, target_tokens, *, keep=None, n_keep=None,
+                          next_token=None, status=None, stream=None):
+    """``ddtree_accept_compact_layers``: acceptance once, then the compaction of every layer's
+    ``(ckv, kpe)``.  ``prefix`` is an int (every stream) or a device int32 ``[S]`` tensor, which the
+    call advances by each stream's accepted count.  Returns ``(keep, n_keep, next_token)``."""
+    table, s = _layer_table(caches)
+    s2, q, keep, n_keep, next_token = _accept_inputs(parents, draft_tokens, target_tokens, keep, n_keep,
+                                                     next_token, status)
+    if s2 != s:
+        raise ValueError("shape mismatch")
+    p, pl = _prefix_arg(prefix, s)
+    _check(LIB.ddtree_accept_compact_layers(table, len(table), p, pl, _ptr(parents), _ptr(draft_tokens),
+                                            _ptr(target_tokens), int(q), _ptr(keep), int(keep.shape[1]),
+                                            _ptr(n_keep), _ptr(next_token), _ptr(status), _stream(stream)))
     return keep, n_keep, next_token
 
 

@@ -14,6 +14,8 @@
 
 #include "kernels.h"
 
+#include "../../include/ddtree.h"
+
 namespace ddtree {
 
 constexpr int kCompactThreads = 256;
@@ -22,14 +24,18 @@ constexpr int kChunksRope = kDRope * 2 / 16;  // 8 chunks per rotary row
 constexpr int kChunksRow = kChunksLat + kChunksRope;
 constexpr int kCompactPerThread = (kMaxQ * kChunksRow + kCompactThreads - 1) / kCompactThreads;  // 18
 
+// 16-byte chunk as a native vector: an array of these stays in VGPRs (HIP's uint4 is a struct
+// with a union, which keeps the array below in scratch memory and serialises its loads).
+typedef unsigned int Chunk16 __attribute__((ext_vector_type(4)));
+
 // Moves rows row0 + keep_s[i] to row0 + i for i < n (n <= kMaxQ, keep_s strictly increasing, in
 // LDS and visible to every thread).  Called by all kCompactThreads threads of the workgroup.
 __device__ __forceinline__ void compact_rows(uint16_t* ckv16, uint16_t* kpe16, size_t row0, const int* keep_s, int n) {
   const int tid = threadIdx.x;
-  uint4* ckv = reinterpret_cast<uint4*>(ckv16);
-  uint4* kpe = reinterpret_cast<uint4*>(kpe16);
+  Chunk16* ckv = reinterpret_cast<Chunk16*>(ckv16);
+  Chunk16* kpe = reinterpret_cast<Chunk16*>(kpe16);
   const int total = n * kChunksRow;
-  uint4 v[kCompactPerThread];
+  Chunk16 v[kCompactPerThread];
 #pragma unroll
   for (int j = 0; j < kCompactPerThread; ++j) {
     const int c = tid + j * kCompactThreads;
@@ -60,6 +66,29 @@ __device__ __forceinline__ void compact_rows(uint16_t* ckv16, uint16_t* kpe16, s
       }
     }
   }
+}
+
+// Reads a caller-given keep row (n entries) into keep_s and checks it against the stream's prefix
+// P: n in [0, min(keep_stride, kMaxQ)], P in [0, kv_rows], entries strictly increasing, first
+// >= 0, last row P + keep[n-1] < kv_rows.  Returns 0 when the gather may run, else the status
+// bit that says why not.  Called by every thread of the workgroup with the same n and P; the
+// result is uniform.  bad_s is a workgroup-shared int.
+__device__ __forceinline__ int load_keep(const int32_t* keep_row, int n, int keep_stride, int P, int kv_rows,
+                                         int* keep_s, int* bad_s) {
+  const int tid = threadIdx.x;
+  if (n < 0 || n > keep_stride || n > kMaxQ) return DDTREE_STATUS_BAD_KEEP;
+  if (P < 0 || P > kv_rows) return DDTREE_STATUS_BAD_PREFIX;
+  if (tid == 0) *bad_s = 0;
+  __syncthreads();
+  if (tid < n) {
+    const int k = keep_row[tid];
+    bool ok = k >= 0 && (long long)P + k < (long long)kv_rows;
+    if (tid > 0) ok = ok && keep_row[tid - 1] < k;
+    keep_s[tid] = k;
+    if (!ok) *bad_s = 1;
+  }
+  __syncthreads();
+  return *bad_s ? DDTREE_STATUS_BAD_KEEP : 0;
 }
 
 }  // namespace ddtree

@@ -466,6 +466,108 @@ int ddtree_accept_compact_ragged(const ddtree_kv_cache* cache, int32_t* prefix_l
                              n_keep, next_token, dev_status, stream);
 }
 
+namespace {
+
+// Shared checks of the multi-layer calls: the layer table, its common geometry, alignment, and
+// that no two caches (and no cache and small array) overlap.  Fills the pointer tables of `a`.
+int check_layers(const ddtree_kv_cache* caches, int n_layers, const Range* small, int n_small,
+                 ddtree::LayersArgs* a) {
+  if (!caches) return DDTREE_ERR_NULL;
+  if (n_layers < 1 || n_layers > ddtree::kMaxLayers) return DDTREE_ERR_SHAPE;
+  const int kv_rows = caches[0].kv_rows, n_streams = caches[0].n_streams;
+  if (kv_rows < 1 || n_streams < 1) return DDTREE_ERR_SHAPE;
+  Range r[2 * ddtree::kMaxLayers];
+  for (int l = 0; l < n_layers; ++l) {
+    const ddtree_kv_cache& c = caches[l];
+    if (!c.ckv || !c.kpe) return DDTREE_ERR_NULL;
+    if (c.kv_rows != kv_rows || c.n_streams != n_streams) return DDTREE_ERR_SHAPE;
+    if (!aligned16(c.ckv) || !aligned16(c.kpe)) return DDTREE_ERR_ALIGN;
+    r[2 * l] = range_of(c.ckv, (size_t)n_streams * kv_rows * kDLat * 2);
+    r[2 * l + 1] = range_of(c.kpe, (size_t)n_streams * kv_rows * kDRope * 2);
+    a->ckv[l] = static_cast<uint16_t*>(c.ckv);
+    a->kpe[l] = static_cast<uint16_t*>(c.kpe);
+  }
+  for (int i = 0; i < 2 * n_layers; ++i) {
+    for (int j = i + 1; j < 2 * n_layers; ++j)
+      if (overlap(r[i], r[j])) return DDTREE_ERR_ALIAS;
+    for (int k = 0; k < n_small; ++k)
+      if (overlap(r[i], small[k])) return DDTREE_ERR_ALIAS;
+  }
+  a->kv_rows = kv_rows;
+  a->n_streams = n_streams;
+  a->n_layers = n_layers;
+  return DDTREE_OK;
+}
+
+}  // namespace
+
+int ddtree_compact_kv_layers(const ddtree_kv_cache* caches, int n_layers, int prefix_len, const int32_t* prefix_lens,
+                             const int32_t* keep, const int32_t* n_keep, int keep_stride, int32_t* dev_status,
+                             hipStream_t stream) {
+  if (!caches || !keep || !n_keep) return DDTREE_ERR_NULL;
+  if (keep_stride < 1 || (!prefix_lens && prefix_len < 0)) return DDTREE_ERR_SHAPE;
+  if (!aligned4(keep) || !aligned4(n_keep) || (dev_status && !aligned4(dev_status)) ||
+      (prefix_lens && !aligned4(prefix_lens)))
+    return DDTREE_ERR_ALIGN;
+  const int n_streams = caches[0].n_streams;
+  if (n_streams < 1) return DDTREE_ERR_SHAPE;
+  const Range small[4] = {range_of(keep, (size_t)n_streams * keep_stride * 4), range_of(n_keep, (size_t)n_streams * 4),
+                          range_of(prefix_lens, prefix_lens ? (size_t)n_streams * 4 : 0),
+                          range_of(dev_status, dev_status ? 4 : 0)};
+  ddtree::LayersArgs a{};
+  const int rc = check_layers(caches, n_layers, small, 4, &a);
+  if (rc != DDTREE_OK) return rc;
+  if (!prefix_lens && prefix_len > a.kv_rows) return DDTREE_ERR_SHAPE;
+  a.keep = const_cast<int32_t*>(keep);  // read only in this call
+  a.n_keep = const_cast<int32_t*>(n_keep);
+  a.status = dev_status;
+  a.prefix_lens = const_cast<int32_t*>(prefix_lens);
+  a.prefix_len = prefix_lens ? 0 : prefix_len;
+  a.keep_stride = keep_stride;
+  if (ddtree::launch_compact_layers(a, stream) != hipSuccess) return DDTREE_ERR_HIP;
+  return DDTREE_OK;
+}
+
+int ddtree_accept_compact_layers(const ddtree_kv_cache* caches, int n_layers, int prefix_len, int32_t* prefix_lens,
+                                 const int32_t* parents, const int32_t* draft_tokens, const int32_t* target_tokens,
+                                 int q_len, int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
+                                 int32_t* dev_status, hipStream_t stream) {
+  if (!caches) return DDTREE_ERR_NULL;
+  const int n_streams = caches[0].n_streams;
+  if (n_streams < 1) return DDTREE_ERR_SHAPE;
+  int rc = check_accept(parents, draft_tokens, target_tokens, q_len, n_streams, keep, keep_stride, n_keep,
+                        next_token, dev_status);
+  if (rc != DDTREE_OK) return rc;
+  if (prefix_lens && !aligned4(prefix_lens)) return DDTREE_ERR_ALIGN;
+  const size_t in_bytes = (size_t)n_streams * q_len * 4;
+  const Range small[8] = {range_of(parents, in_bytes), range_of(draft_tokens, in_bytes),
+                          range_of(target_tokens, in_bytes), range_of(keep, (size_t)n_streams * keep_stride * 4),
+                          range_of(n_keep, (size_t)n_streams * 4),
+                          range_of(next_token, next_token ? (size_t)n_streams * 4 : 0),
+                          range_of(dev_status, dev_status ? 4 : 0),
+                          range_of(prefix_lens, prefix_lens ? (size_t)n_streams * 4 : 0)};
+  for (int o = 0; o < 7; ++o)
+    if (overlap(small[o], small[7])) return DDTREE_ERR_ALIAS;
+  ddtree::LayersArgs a{};
+  rc = check_layers(caches, n_layers, small, 8, &a);
+  if (rc != DDTREE_OK) return rc;
+  const int p0 = prefix_lens ? 0 : prefix_len;
+  if (p0 < 0 || (long long)p0 + q_len > (long long)a.kv_rows) return DDTREE_ERR_SHAPE;
+  a.parents = parents;
+  a.draft = draft_tokens;
+  a.target = target_tokens;
+  a.keep = keep;
+  a.n_keep = n_keep;
+  a.next_token = next_token;
+  a.status = dev_status;
+  a.prefix_lens = prefix_lens;
+  a.prefix_len = p0;
+  a.q_len = q_len;
+  a.keep_stride = keep_stride;
+  if (ddtree::launch_accept_compact_layers(a, stream) != hipSuccess) return DDTREE_ERR_HIP;
+  return DDTREE_OK;
+}
+
 int ddtree_tree_build(const float* logprobs, const int32_t* topk_tokens, const int32_t* root_tokens, int depth,
                       int topk, int budget, int n_streams, int32_t* parents, int32_t* node_tokens,
                       int32_t* n_nodes, int32_t* depths, float* logw, int32_t* first_child,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/ddtree.h"
+
 namespace ddtree {
 
 constexpr int kHeads = 64;
@@ -117,5 +119,34 @@ struct BuildArgs {
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_accept_compact(const AcceptArgs& a, hipStream_t stream);
+
+// Compaction of every layer's cache in one launch.  All layers share n_streams and kv_rows;
+// workgroup (s, layer) = (blockIdx.x, blockIdx.y).  The pointer tables travel in the kernel
+// arguments (2 KB at kMaxLayers = 128).
+constexpr int kMaxLayers = DDTREE_MAX_LAYERS;
+
+struct LayersArgs {
+  uint16_t* ckv[kMaxLayers];
+  uint16_t* kpe[kMaxLayers];
+  const int32_t* parents;  // acceptance: [n_streams][q_len] (with draft / target)
+  const int32_t* draft;
+  const int32_t* target;
+  int32_t* keep;           // [n_streams][keep_stride]: written by acceptance, else read
+  int32_t* n_keep;         // [n_streams]: written by acceptance, else read
+  int32_t* next_token;     // acceptance only, or null
+  int32_t* status;         // or null
+  int32_t* prefix_lens;    // per stream, or null: prefix_len for every stream
+  int kv_rows;
+  int prefix_len;
+  int q_len;               // acceptance only
+  int n_streams;
+  int keep_stride;
+  int n_layers;
+};
+
+// keep / n_keep given: validated per stream, then gathered in every layer.
+hipError_t launch_compact_layers(const LayersArgs& a, hipStream_t stream);
+// Acceptance, then the gather in every layer; with prefix_lens, a second launch advances them.
+hipError_t launch_accept_compact_layers(const LayersArgs& a, hipStream_t stream);
 
 }  // namespace ddtree
