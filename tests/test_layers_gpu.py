@@ -135,3 +135,28 @@ def test_one_layer_equals_single_cache_call(lib):
     assert torch.equal(c1, c2) and torch.equal(k1, k2)
     for a, b2 in zip(o1, o2):
         assert torch.equal(a, b2)
+
+
+def test_grouped_layers_and_long_paths(lib):
+    """Enough (stream, layer) pairs that each workgroup takes several layers, with paths from one
+    row to 64 rows: a full 64-node chain moves 63 rows per layer, one layer per register round;
+    short paths fit many layers in one round."""
+    n_layers, s_count, q, prefix = 128, 32, 64, 10
+    parents, draft, target = trees(101, s_count, q)
+    parents[0] = np.arange(-1, q - 1)                   # full chain, accepted to the end
+    draft[0] = np.arange(q)
+    target[0] = np.arange(1, q + 1)
+    parents[1], draft[1], target[1] = parents[0], draft[0], np.zeros(q, np.int32)  # root only
+    host = synth.layer_caches(102, n_layers, s_count, prefix + q + 1)
+    dev = upload(host)
+    print(f"[layers] grouped L={n_layers} S={s_count} Q={q}", flush=True)
+    keep, n_keep, _ = lib.accept_compact_layers(dev, prefix, dev_i32(parents), dev_i32(draft), dev_i32(target))
+    torch.cuda.synchronize()
+    rk, rn, _ = oracle.tree_accept_streams(parents, draft, target)
+    assert rn[0] == q and rn[1] == 1
+    assert np.array_equal(n_keep.cpu().numpy(), rn)
+    check_layers(dev, host, [prefix] * s_count, rk, rn, "grouped accept")
+    dev = upload(host)
+    lib.compact_kv_layers(dev, prefix, dev_i32(rk), dev_i32(rn))
+    torch.cuda.synchronize()
+    check_layers(dev, host, [prefix] * s_count, rk, rn, "grouped compact")

@@ -32,7 +32,7 @@ __global__ void __launch_bounds__(64) tree_accept_kernel(AcceptArgs a) {
 // accepted rows are committed, and the next tree goes after them.
 __global__ void __launch_bounds__(kCompactThreads) accept_compact_kernel(AcceptArgs a) {
   __shared__ int keep_s[kMaxQ];
-  __shared__ int n_s;
+  __shared__ int n_s, first_s;
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   const int P = a.prefix_lens != nullptr ? a.prefix_lens[s] : a.prefix_len;
@@ -40,7 +40,11 @@ __global__ void __launch_bounds__(kCompactThreads) accept_compact_kernel(AcceptA
     const Walk w = accept_walk(a.parents, a.draft, a.target, a.q_len, s, tid);
     write_outputs(a, s, tid, w);
     if (tid < w.n) keep_s[tid] = w.my_node;
-    if (tid == 0) n_s = w.n;
+    const int first = rows_in_place(w.my_node, tid, w.n);
+    if (tid == 0) {
+      n_s = w.n;
+      first_s = first;
+    }
   }
   __syncthreads();
   const int n = n_s;
@@ -49,7 +53,7 @@ __global__ void __launch_bounds__(kCompactThreads) accept_compact_kernel(AcceptA
     if (tid == 0 && a.status != nullptr) atomicOr(a.status, DDTREE_STATUS_BAD_PREFIX);
     return;
   }
-  compact_rows(a.ckv, a.kpe, (size_t)s * a.kv_rows + P, keep_s, n);
+  compact_rows(a.ckv, a.kpe, (size_t)s * a.kv_rows + P, keep_s, first_s, n);
   if (a.prefix_lens != nullptr && tid == 0) a.prefix_lens[s] = P + n;
 }
 

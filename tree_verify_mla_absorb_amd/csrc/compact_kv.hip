@@ -11,16 +11,17 @@ namespace {
 
 __global__ void __launch_bounds__(kCompactThreads) compact_kv_kernel(CompactArgs a) {
   __shared__ int keep_s[kMaxQ];
-  __shared__ int bad_s;
+  __shared__ int bad_s, first_s;
   const int s = blockIdx.x;
   const int P = a.prefix_lens != nullptr ? a.prefix_lens[s] : a.prefix_len;
   const int n = a.n_keep[s];
-  const int why = load_keep(a.keep + (size_t)s * a.keep_stride, n, a.keep_stride, P, a.kv_rows, keep_s, &bad_s);
+  const int why = load_keep(a.keep + (size_t)s * a.keep_stride, n, a.keep_stride, P, a.kv_rows, keep_s, &bad_s,
+                            &first_s);
   if (why != 0) {
     if (threadIdx.x == 0 && a.status != nullptr) atomicOr(a.status, why);
     return;
   }
-  compact_rows(a.ckv, a.kpe, (size_t)s * a.kv_rows + P, keep_s, n);
+  compact_rows(a.ckv, a.kpe, (size_t)s * a.kv_rows + P, keep_s, first_s, n);
 }
 
 }  // namespace

@@ -496,6 +496,12 @@ int check_layers(const ddtree_kv_cache* caches, int n_layers, const Range* small
   a->kv_rows = kv_rows;
   a->n_streams = n_streams;
   a->n_layers = n_layers;
+  // Layers per workgroup: about four resident workgroups per compute unit in all, so that the
+  // whole grid is in flight at once and each workgroup pays the load -> barrier -> store latency
+  // about once.
+  const long long target = 4LL * cu_count();
+  const long long per = ((long long)n_layers * n_streams + target - 1) / target;
+  a->layers_per_wg = (int)(per < 1 ? 1 : (per > n_layers ? n_layers : per));
   return DDTREE_OK;
 }
 

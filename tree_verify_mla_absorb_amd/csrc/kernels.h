@@ -121,8 +121,8 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_accept_compact(const AcceptArgs& a, hipStream_t stream);
 
 // Compaction of every layer's cache in one launch.  All layers share n_streams and kv_rows;
-// workgroup (s, layer) = (blockIdx.x, blockIdx.y).  The pointer tables travel in the kernel
-// arguments (2 KB at kMaxLayers = 128).
+// workgroup (s, group) = (blockIdx.x, blockIdx.y) handles layers [group * layers_per_wg, ...).
+// The pointer tables travel in the kernel arguments (2 KB at kMaxLayers = 128).
 constexpr int kMaxLayers = DDTREE_MAX_LAYERS;
 
 struct LayersArgs {
@@ -142,6 +142,7 @@ struct LayersArgs {
   int n_streams;
   int keep_stride;
   int n_layers;
+  int layers_per_wg;
 };
 
 // keep / n_keep given: validated per stream, then gathered in every layer.
