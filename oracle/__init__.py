@@ -10,6 +10,8 @@ Everything is written out from its definition, in float64, with no blocking or f
 * ``compact_kv``    -- the out-of-place gather of the kept tree rows into the prefix.
 * ``tree_accept``   -- the greedy walk that picks the accepted path (the rows to keep).
 * ``tree_build``    -- the best-first expansion of the drafter's top-k into the draft tree.
+* ``append_tree_kv`` -- the tree's cache rows: RMSNorm of the latent part, NeoX rotation of the
+  rotary part at each node's position, rounded to bf16, written at the tree's offset.
 
 Every function is pinned by the CPU tests (brute force over all small trees, causal attention
 for a chain, per-path causal attention, closed forms, lse merge, equivariances, the absorb
@@ -31,3 +33,4 @@ from .verify import (  # noqa: F401
 from .compact import compact_kv, compact_kv_ragged, validate_keep  # noqa: F401
 from .accept import tree_accept, tree_accept_streams, validate_parents  # noqa: F401
 from .build import tree_build  # noqa: F401
+from .append import append_tree_kv, bf16_round_bits, rms_norm, rope_neox, tree_depths, tree_rows  # noqa: F401

@@ -32,6 +32,7 @@ MAX_DEPTH = 15
 TAG_Q_LAT, TAG_Q_PE, TAG_CKV, TAG_KPE, TAG_PARENTS, TAG_LEAF = 0, 1, 2, 3, 4, 5
 TAG_DRAFT_TOK, TAG_TARGET_TOK, TAG_ACCEPT_DEPTH, TAG_DRAFTER = 6, 7, 8, 9
 TAG_LAYER_CKV, TAG_LAYER_KPE = 10, 11
+TAG_KV_PROJ, TAG_NORM_W = 12, 13
 VOCAB = 163840  # synthetic vocabulary size for token ids
 
 
@@ -244,3 +245,22 @@ def layer_caches(seed: int, n_layers: int, streams: int, rows: int):
                 [seed, s, TAG_LAYER_KPE, layer]))), (rows, D_ROPE))
         out.append((ckv, kpe))
     return out
+
+
+def rope_tables(rows: int, base: float = 10000.0):
+    """The caller's rotary tables, float32 ``[rows, 32]`` each: angle ``pos * base**(-j / 32)``
+    for the 32 rotated pairs of a 64-value rotary row (the usual frequency ladder)."""
+    inv = base ** (-np.arange(32, dtype=np.float64) / 32.0)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def append_inputs(seed: int, streams: int, q_len: int):
+    """Inputs of the tree-row append: the key/value projection's float32 output ``[streams,
+    q_len, 576]`` (standard normal, scaled by 2 so that the norm has work to do) and the
+    RMSNorm weight ``[512]`` (uniform in [0.5, 1.5])."""
+    kv = np.empty((streams, q_len, D_LATENT + D_ROPE), np.float32)
+    for s in range(streams):
+        kv[s] = 2.0 * rng_for(seed, s, TAG_KV_PROJ).standard_normal((q_len, D_LATENT + D_ROPE), dtype=np.float32)
+    w = rng_for(seed, 0, TAG_NORM_W).uniform(0.5, 1.5, D_LATENT).astype(np.float32)
+    return kv, w
