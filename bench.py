@@ -195,6 +195,22 @@ def layers_table(lib, dev, w, parents, draft_tok, target_tok, keep_bits, n_keep_
             "moved_bytes": moved_bytes, "gbs": round(moved_bytes / (fused * 1e-6) / 1e9, 1)}
 
 
+def append_table(lib, dev, w, parents):
+    """``ddtree_append_tree_kv`` us/call on the workload's trees: the projection's fp32 rows in,
+    the bf16 cache rows out, at the workload's prefix (tables cover the positions)."""
+    import torch
+    import synth
+    kv, nw = synth.append_inputs(7, w.streams, w.q_len)
+    cos, sin = synth.rope_tables(w.prefix + w.q_len)
+    kv_d, nw_d = torch.from_numpy(kv).to(dev), torch.from_numpy(nw).to(dev)
+    cos_d, sin_d = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
+    ckv = torch.empty((w.streams, w.kv_rows, 512), dtype=torch.bfloat16, device=dev)
+    kpe = torch.empty((w.streams, w.kv_rows, 64), dtype=torch.bfloat16, device=dev)
+    us = time_calls(lambda: lib.append_tree_kv(ckv, kpe, w.prefix, parents, kv_d, nw_d, 1e-6, cos_d, sin_d))
+    nbytes = w.streams * w.q_len * (576 * 4 + 576 * 2)  # fp32 rows in, bf16 rows out
+    return {"us_per_call": round(us, 2), "bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def _db_rows(path: str, sql: str):
     import sqlite3
     con = sqlite3.connect(path)
@@ -356,6 +372,7 @@ def main() -> int:
                                                       n_keep=n_keep, next_token=next_tok))
     compact_us = time_calls(lambda: _lib.compact_kv(ckv, kpe, w.prefix, keep, n_keep))
     layers = layers_table(_lib, dev, w, parents, draft_tok, target_tok, b.keep, b.n_keep)
+    append = append_table(_lib, dev, w, parents)
 
     flops = 2.0 * w.heads * (576 + 512) * visible_pairs(b.parents, w.prefix)
     tflops_step = flops / (ms_step * 1e-3) / 1e12
@@ -386,6 +403,7 @@ def main() -> int:
                    "tree_accept_us_per_call": accept_us,
                    "tree_build_us_per_call": build_us,
                    "accept_compact_layers": layers,
+                   "append_tree_kv": append,
                    "verify_tflops": round(achieved, 2),
                    "pct_mfma_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
                    "algorithmic_bytes": algorithmic_bytes(w, w.streams),

@@ -17,6 +17,7 @@
  *   ddtree_accept_compact  acceptance and compaction in one launch;
  *   ddtree_compact_kv_layers, ddtree_accept_compact_layers
  *                        the same for every layer's cache of a model, in one launch;
+ *   ddtree_append_tree_kv  the tree's rows written into the cache at the tree's offset;
  *
  * and the step before them, described on "Building the Foundation: Architecting a Native CUDA
  * DDTree Inference Engine":
@@ -74,6 +75,7 @@ extern "C" {
                                        ancestor walk stops there                               */
 #define DDTREE_STATUS_BAD_KEEP 2    /* keep[]/n_keep of a stream invalid; that stream untouched */
 #define DDTREE_STATUS_BAD_PREFIX 4  /* a per-stream prefix length out of range; see the ragged calls */
+#define DDTREE_STATUS_BAD_POSITION 8 /* a tree position past the rotary tables; see ddtree_append_tree_kv */
 
 /*
  * ddtree_verify_attn -- tree-verify attention, absorbed MLA form, one launch for all streams.
@@ -295,6 +297,40 @@ int ddtree_accept_compact_layers(const ddtree_kv_cache* caches, int n_layers, in
                                  const int32_t* parents, const int32_t* draft_tokens, const int32_t* target_tokens,
                                  int q_len, int32_t* keep, int keep_stride, int32_t* n_keep, int32_t* next_token,
                                  int32_t* dev_status, hipStream_t stream);
+
+/*
+ * ddtree_append_tree_kv -- the draft tree's cache rows, written straight into the cache at the
+ * tree's offset ("Race Conditions, Buffer Aliasing, and the Architecture of a Native DDTree
+ * Inference Engine", section "Scratch Buffer Architecture: Managing Transformer Activations":
+ * the key/value projection's output goes through RMSNorm directly into the cache; the model is
+ * MLA with RMSNorm and NeoX rotary embeddings per section "Assumptions, Input Knowledge, and
+ * Output Knowledge").
+ *
+ * For every stream s (P = prefix_lens[s], or prefix_len when prefix_lens is NULL) and tree node
+ * i < q_len, with x = kv[s][i] (576 fp32: 512 latent, then 64 rotary) and pos = P + depth(i):
+ *   ckv[s][P + i][k]    = bf16( x[k] / sqrt(mean_k'(x[k']^2) + eps) * norm_weight[k] ), k < 512
+ *   kpe[s][P + i][j]    = bf16( x[512 + j] cos[pos][j] - x[544 + j] sin[pos][j] ),    j < 32
+ *   kpe[s][P + i][32+j] = bf16( x[544 + j] cos[pos][j] + x[512 + j] sin[pos][j] )
+ * rounded to nearest, ties to even; the sums are computed in fp32.  depth(root) = 0, so the root
+ * sits at position P, right after the P committed rows; siblings share a position.  No other
+ * cache row is touched.
+ *
+ * Arguments (device pointers):
+ *   cache        the latent cache (as for ddtree_compact_kv); written
+ *   parents      int32 [n_streams][q_len], parents[s][0] = -1, else an earlier node
+ *   kv           fp32 [n_streams][q_len][576], 16-byte aligned
+ *   norm_weight  fp32 [512], 16-byte aligned
+ *   rope_cos     fp32 [rope_rows][32], rope_sin likewise (4-byte aligned)
+ *   eps          >= 0, finite
+ * Requires 1 <= q_len <= 64 and, with one prefix_len, prefix_len + q_len <= kv_rows.
+ * A stream with a malformed tree (DDTREE_STATUS_BAD_PARENTS), a block outside the cache
+ * (DDTREE_STATUS_BAD_PREFIX) or a position >= rope_rows (DDTREE_STATUS_BAD_POSITION) is left
+ * untouched and flagged in dev_status.
+ */
+int ddtree_append_tree_kv(const ddtree_kv_cache* cache, int prefix_len, const int32_t* prefix_lens,
+                          const int32_t* parents, int q_len, const float* kv, const float* norm_weight, float eps,
+                          const float* rope_cos, const float* rope_sin, int rope_rows, int32_t* dev_status,
+                          hipStream_t stream);
 
 /*
  * ddtree_tree_build -- best-first draft trees, one launch for all requests (streams).

@@ -246,3 +246,26 @@ def test_layers_prefix_bounds():
     assert accept_layers(prefix_lens=D + 8) == _lib.ERR_ALIAS    # prefix_lens inside keep
     assert compact_layers(keep=None) == _lib.ERR_NULL
     assert accept_layers(parents=None) == _lib.ERR_NULL
+
+
+def append(prefix=100, prefix_lens=None, parents=A, q=9, kv=B, w=C, eps=1e-6, cos=D, sin=E, rope_rows=4096,
+           status=None, cache=True, rows=300, s=2):
+    c = _lib.KVCache(G, G + 0x10000000, rows, s)
+    return _lib.LIB.ddtree_append_tree_kv(ctypes.byref(c) if cache else None, prefix, prefix_lens, parents, q, kv, w,
+                                          eps, cos, sin, rope_rows, status, None)
+
+
+def test_append_argument_errors():
+    assert append(cache=False) == _lib.ERR_NULL
+    for field in ("parents", "kv", "w", "cos", "sin"):
+        assert append(**{field: None}) == _lib.ERR_NULL
+    for kw in (dict(q=0), dict(q=65), dict(s=0), dict(rope_rows=0), dict(eps=-1.0), dict(eps=float("inf")),
+               dict(eps=float("nan")), dict(prefix=292), dict(prefix=-1), dict(rows=8, prefix_lens=F)):
+        assert append(**kw) == _lib.ERR_SHAPE, kw
+    assert append(kv=B + 4) == _lib.ERR_ALIGN
+    assert append(w=C + 8) == _lib.ERR_ALIGN
+    assert append(cos=D + 2) == _lib.ERR_ALIGN
+    assert append(prefix_lens=F + 2) == _lib.ERR_ALIGN
+    assert append(kv=G + 0x10000000 + 64) == _lib.ERR_ALIAS   # kv inside the rotary cache
+    assert append(cos=G + 1024) == _lib.ERR_ALIAS              # table inside the latent cache
+    assert append(status=B + 16) == _lib.ERR_ALIAS             # status word inside kv

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     accept_compact,
     accept_compact_layers,
     accept_compact_ragged,
+    append_tree_kv,
     compact_kv,
     compact_kv_layers,
     compact_kv_ragged,

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libddtree.so")
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = -1, -2, -3, -4, -5, -6
-STATUS_BAD_PARENTS, STATUS_BAD_KEEP, STATUS_BAD_PREFIX = 1, 2, 4
+STATUS_BAD_PARENTS, STATUS_BAD_KEEP, STATUS_BAD_PREFIX, STATUS_BAD_POSITION = 1, 2, 4, 8
 HEADS, D_LATENT, D_ROPE, MAX_Q_LEN, MAX_LAYERS = 64, 512, 64, 64, 128
 
 
@@ -53,6 +53,8 @@ def _load() -> ctypes.CDLL:
     lib.ddtree_compact_kv_layers.restype = i32
     lib.ddtree_accept_compact_layers.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp]
     lib.ddtree_accept_compact_layers.restype = i32
+    lib.ddtree_append_tree_kv.argtypes = [vp, i32, vp, vp, i32, vp, vp, f32, vp, vp, i32, vp, vp]
+    lib.ddtree_append_tree_kv.restype = i32
     lib.ddtree_status_string.argtypes = [i32]
     lib.ddtree_status_string.restype = ctypes.c_char_p
     lib.ddtree_version.argtypes = []
@@ -76,6 +78,7 @@ EXPORTED = (
     "ddtree_tree_build",
     "ddtree_compact_kv_layers",
     "ddtree_accept_compact_layers",
+    "ddtree_append_tree_kv",
     "ddtree_status_string",
     "ddtree_version",
 )
@@ -375,6 +378,33 @@ def accept_compact_layers(caches, prefix, parents, draft_tokens, target_tokens, 
                                             _ptr(target_tokens), int(q), _ptr(keep), int(keep.shape[1]),
                                             _ptr(n_keep), _ptr(next_token), _ptr(status), _stream(stream)))
     return keep, n_keep, next_token
+
+
+def append_tree_kv(ckv, kpe, prefix, parents, kv, norm_weight, eps: float, rope_cos, rope_sin, *, status=None,
+                   stream=None) -> None:
+    """``ddtree_append_tree_kv``: write every stream's tree rows into ``ckv [S, rows, 512]`` /
+    ``kpe [S, rows, 64]`` at ``prefix`` (an int, or a device int32 ``[S]``): RMSNorm of
+    ``kv [S, Q, 576]``'s latent part with ``norm_weight [512]``, NeoX rotation of its rotary part
+    by ``rope_cos`` / ``rope_sin [rows, 32]`` at position prefix + depth (all fp32)."""
+    _need(ckv, "ckv", _BF16)
+    _need(kpe, "kpe", _BF16)
+    _need(parents, "parents", (torch.int32,))
+    for t, name in ((kv, "kv"), (norm_weight, "norm_weight"), (rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        _need(t, name, (torch.float32,))
+    if status is not None:
+        _need(status, "status", (torch.int32,))
+    s, rows = ckv.shape[0], ckv.shape[1]
+    if parents.dim() != 2 or parents.shape[0] != s:
+        raise ValueError("parents must be [S, Q]")
+    q = parents.shape[1]
+    if kpe.shape[:2] != (s, rows) or kv.shape != (s, q, D_LATENT + D_ROPE) or norm_weight.shape != (D_LATENT,) \
+            or rope_cos.dim() != 2 or rope_cos.shape[1] != 32 or rope_sin.shape != rope_cos.shape:
+        raise ValueError("shape mismatch")
+    p, pl = _prefix_arg(prefix, s)
+    cache = KVCache(ckv.data_ptr(), kpe.data_ptr(), int(rows), int(s))
+    _check(LIB.ddtree_append_tree_kv(ctypes.byref(cache), p, pl, _ptr(parents), int(q), _ptr(kv), _ptr(norm_weight),
+                                     float(eps), _ptr(rope_cos), _ptr(rope_sin), int(rope_cos.shape[0]),
+                                     _ptr(status), _stream(stream)))
 
 
 def tree_build(logprobs, topk_tokens, budget: int, *, root_tokens=None, extras: bool = False, stream=None):

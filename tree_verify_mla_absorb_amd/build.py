@@ -17,7 +17,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["verify_attn.hip", "compact_kv.hip", "accept.hip", "compact_layers.hip", "build_tree.hip", "ddtree_api.hip"]
+SOURCES = ["verify_attn.hip", "compact_kv.hip", "accept.hip", "compact_layers.hip", "append_kv.hip", "build_tree.hip", "ddtree_api.hip"]
 LIB = os.path.join(PKG, "libddtree.so")
 ARCH = "gfx950"
 

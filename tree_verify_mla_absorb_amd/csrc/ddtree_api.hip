@@ -574,6 +574,53 @@ int ddtree_accept_compact_layers(const ddtree_kv_cache* caches, int n_layers, in
   return DDTREE_OK;
 }
 
+int ddtree_append_tree_kv(const ddtree_kv_cache* cache, int prefix_len, const int32_t* prefix_lens,
+                          const int32_t* parents, int q_len, const float* kv, const float* norm_weight, float eps,
+                          const float* rope_cos, const float* rope_sin, int rope_rows, int32_t* dev_status,
+                          hipStream_t stream) {
+  if (!cache || !cache->ckv || !cache->kpe || !parents || !kv || !norm_weight || !rope_cos || !rope_sin)
+    return DDTREE_ERR_NULL;
+  const int S = cache->n_streams;
+  if (S < 1 || cache->kv_rows < 1 || q_len < 1 || q_len > kMaxQ || q_len > cache->kv_rows || rope_rows < 1 ||
+      !(eps >= 0.f) || !isfinite(eps))
+    return DDTREE_ERR_SHAPE;
+  if (!prefix_lens && (prefix_len < 0 || (long long)prefix_len + q_len > (long long)cache->kv_rows))
+    return DDTREE_ERR_SHAPE;
+  if (!aligned16(cache->ckv) || !aligned16(cache->kpe) || !aligned16(kv) || !aligned16(norm_weight) ||
+      !aligned4(rope_cos) || !aligned4(rope_sin) || !aligned4(parents) || (prefix_lens && !aligned4(prefix_lens)) ||
+      (dev_status && !aligned4(dev_status)))
+    return DDTREE_ERR_ALIGN;
+  const Range ckv = range_of(cache->ckv, (size_t)S * cache->kv_rows * kDLat * 2);
+  const Range kpe = range_of(cache->kpe, (size_t)S * cache->kv_rows * kDRope * 2);
+  if (overlap(ckv, kpe)) return DDTREE_ERR_ALIAS;
+  const Range ins[7] = {range_of(kv, (size_t)S * q_len * (kDLat + kDRope) * 4), range_of(norm_weight, kDLat * 4),
+                        range_of(rope_cos, (size_t)rope_rows * 32 * 4), range_of(rope_sin, (size_t)rope_rows * 32 * 4),
+                        range_of(parents, (size_t)S * q_len * 4),
+                        range_of(prefix_lens, prefix_lens ? (size_t)S * 4 : 0),
+                        range_of(dev_status, dev_status ? 4 : 0)};
+  for (const Range& r : ins)
+    if (overlap(r, ckv) || overlap(r, kpe)) return DDTREE_ERR_ALIAS;
+  if (overlap(ins[6], ins[0]) || overlap(ins[6], ins[4]) || overlap(ins[6], ins[5])) return DDTREE_ERR_ALIAS;
+  ddtree::AppendArgs a{};
+  a.kv = kv;
+  a.weight = norm_weight;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.parents = parents;
+  a.prefix_lens = prefix_lens;
+  a.ckv = static_cast<uint16_t*>(cache->ckv);
+  a.kpe = static_cast<uint16_t*>(cache->kpe);
+  a.status = dev_status;
+  a.eps = eps;
+  a.prefix_len = prefix_lens ? 0 : prefix_len;
+  a.q_len = q_len;
+  a.n_streams = S;
+  a.kv_rows = cache->kv_rows;
+  a.rope_rows = rope_rows;
+  if (ddtree::launch_append(a, stream) != hipSuccess) return DDTREE_ERR_HIP;
+  return DDTREE_OK;
+}
+
 int ddtree_tree_build(const float* logprobs, const int32_t* topk_tokens, const int32_t* root_tokens, int depth,
                       int topk, int budget, int n_streams, int32_t* parents, int32_t* node_tokens,
                       int32_t* n_nodes, int32_t* depths, float* logw, int32_t* first_child,

@@ -145,6 +145,27 @@ struct LayersArgs {
   int layers_per_wg;
 };
 
+// The tree's cache rows from the key/value projection's output (RMSNorm + NeoX rotation).
+struct AppendArgs {
+  const float* kv;             // [n_streams][q_len][576]
+  const float* weight;         // [512]
+  const float* rope_cos;       // [rope_rows][32]
+  const float* rope_sin;       // [rope_rows][32]
+  const int32_t* parents;      // [n_streams][q_len]
+  const int32_t* prefix_lens;  // per stream, or null: prefix_len
+  uint16_t* ckv;
+  uint16_t* kpe;
+  int32_t* status;             // or null
+  float eps;
+  int prefix_len;
+  int q_len;
+  int n_streams;
+  int kv_rows;
+  int rope_rows;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
 // keep / n_keep given: validated per stream, then gathered in every layer.
 hipError_t launch_compact_layers(const LayersArgs& a, hipStream_t stream);
 // Acceptance, then the gather in every layer; with prefix_lens, a second launch advances them.
