@@ -237,6 +237,9 @@ int verify_impl(const void* q_lat, const void* q_pe, const void* ckv, const void
     a.tiles_per_split[g] = plan.tiles_per_split[g];
   }
   a.wg_count0 = (int)plan.wgs[0];
+  // Half of group 1 (whole groups of 8, one per XCD) goes first: see the kernel's dispatch
+  // order.  Only worth it with enough group-1 workgroups to shift a sizeable set of CUs.
+  a.lead1 = (plan.wgs[0] > 0 && plan.wgs[1] >= 16) ? (int)((plan.wgs[1] / 2) & ~7LL) : 0;
   a.scale_log2e = scale * 1.4426950408889634f;
 
   const size_t need = workspace_bytes_for(plan);

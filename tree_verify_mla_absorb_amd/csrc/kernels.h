@@ -20,7 +20,8 @@ constexpr int kTileKeys = 32;
 constexpr int kWGThreads = 256;
 
 // The launch holds two groups of workgroups.  Group 0: node pairs (2p, 2p + 1), p < q_len / 2.
-// Group 1 (odd q_len only): the last node alone.  Each group has its own key-range split count;
+// Group 1 (odd q_len only): the last node alone.  Dispatch order: lead1 workgroups of group 1,
+// all of group 0, the rest of group 1.  Each group has its own key-range split count;
 // a group with more than one split writes (out, lse) partials that a merge pass combines.
 //   group 0 partial rows: ((s * n_pairs + p) * 2 + node_in_pair) * 64 + head
 //   group 1 partial rows: s * 64 + head
@@ -44,7 +45,8 @@ struct VerifyArgs {
   int n_tiles;         // ceil((prefix_len + q_len) / kTileKeys), the longest stream
   int splits[2];
   int tiles_per_split[2];
-  int wg_count0;       // workgroups of group 0; group 1 follows
+  int wg_count0;       // workgroups of group 0
+  int lead1;           // group-1 workgroups dispatched before group 0 (the rest follow it)
   float scale_log2e;   // softmax scale * log2(e)
 };
 

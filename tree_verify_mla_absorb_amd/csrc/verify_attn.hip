@@ -163,12 +163,17 @@ verify_attn_kernel(VerifyArgs a) {
   const int c32 = lane & 31;
   const int g = lane >> 5;
 
-  // Group and position of this workgroup.  Workgroup b is dispatched to XCD b % 8; within a
-  // group the index is renumbered so that each XCD runs a contiguous run of (stream, node pair,
-  // split) units: the workgroups of one stream then share that XCD's L2 while they stream the
-  // same key tiles, and the light workgroups of group 1 spread over all XCDs.
-  const int grp = (int)blockIdx.x < a.wg_count0 ? 0 : 1;
-  const int j = grp == 0 ? (int)blockIdx.x : (int)blockIdx.x - a.wg_count0;
+  // Group and position of this workgroup.  Dispatch order: the first lead1 workgroups of group
+  // 1, all of group 0, then the rest of group 1.  Workgroups of equal length run in lockstep,
+  // and their Q loads at the start and output stores at the end then hit HBM all at once; the
+  // short group-1 workgroups in front shift half of the compute units by one of them, so the
+  // two halves reach those bursts at different times.  Workgroup b is dispatched to XCD b % 8;
+  // within a group the index is renumbered so that each XCD runs a contiguous run of (stream,
+  // node pair, split) units: the workgroups of one stream then share that XCD's L2 while they
+  // stream the same key tiles, and the light workgroups of group 1 spread over all XCDs.
+  const int b_id = (int)blockIdx.x;
+  const int grp = (b_id >= a.lead1 && b_id < a.lead1 + a.wg_count0) ? 0 : 1;
+  const int j = grp == 0 ? b_id - a.lead1 : (b_id < a.lead1 ? b_id : b_id - a.wg_count0);
   const int cnt = grp == 0 ? a.wg_count0 : (int)gridDim.x - a.wg_count0;
   const int xcd = j & 7;
   const int per = cnt >> 3, rem = cnt & 7;
@@ -199,46 +204,31 @@ verify_attn_kernel(VerifyArgs a) {
   // row of (node q0 + k, head h) in this group's partial buffers
   auto part_row = [&](int k, int h) { return grp == 0 ? ((s * a.n_pairs + pair) * 2 + k) * kHeads + h : s * kHeads + h; };
 
-  // Ancestor-or-self mask of node qc.  Every step must move to a strictly smaller index, so
-  // the walk ends within q_len steps for any input; a malformed entry ends it early.
-  uint64_t anc = 0;
-  bool bad = false;
+  // Ancestor-or-self masks of the whole tree, node j in lane j, from one load of parents[]:
+  // six pointer-jumping steps (mask |= mask[up]; up = up[up]) cover any chain of at most 64
+  // nodes.  A node whose parent entry is not an earlier node (or a root with a parent) links
+  // to itself, so its chain stops there, as a walk that stops at the bad entry would.
+  uint64_t anc;
+  bool bad;
   {
-    const int32_t* par = a.parents + (size_t)s * Q;
-    int node = qc;
-    for (int step = 0; step < Q && node >= 0; ++step) {
-      anc |= 1ull << node;
-      const int pn = par[node];
-      if (pn >= node || pn < -1 || (pn == -1 && node != 0)) {
-        bad = true;
-        node = -1;
-      } else {
-        node = pn;
-      }
+    const bool in = lane < Q;
+    const int pn = in ? a.parents[(size_t)s * Q + lane] : -1;
+    const bool ok = !in || (lane == 0 ? pn == -1 : (pn >= 0 && pn < lane));
+    bad = __builtin_amdgcn_ballot_w64(!ok) != 0;
+    int up = (in && ok && lane != 0) ? pn : lane;
+    unsigned lo = in ? (lane < 32 ? 1u << lane : 0u) : 0u;
+    unsigned hi = in ? (lane >= 32 ? 1u << (lane - 32) : 0u) : 0u;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      lo |= __shfl(lo, up);
+      hi |= __shfl(hi, up);
+      up = __shfl(up, up);
     }
+    anc = (uint64_t)(unsigned)__builtin_amdgcn_readlane((int)lo, qc) |
+          ((uint64_t)(unsigned)__builtin_amdgcn_readlane((int)hi, qc) << 32);
   }
-  if (bad && active && a.status != nullptr && lane == 0) atomicOr(a.status, DDTREE_STATUS_BAD_PARENTS);
+  if (bad && a.status != nullptr && threadIdx.x == 0) atomicOr(a.status, DDTREE_STATUS_BAD_PARENTS);
   if (bad_prefix && a.status != nullptr && threadIdx.x == 0) atomicOr(a.status, DDTREE_STATUS_BAD_PREFIX);
-
-  // Q^T fragments of this wave's head block: lane holds head `head`, dims 16 ks + 8 g .. +7.
-  // The 32 latent k-steps stay in VGPRs for the whole key range; the 4 rotary k-steps are
-  // staged once into LDS (the register file is full: O^T alone takes all 256 AGPRs).
-  const size_t qrow = ((size_t)s * Q + qc) * kHeads + head;
-  bf16x8 qf[32];
-  {
-    const uint16_t* ql = a.q_lat + qrow * kDLat + g * 8;
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(ql + ks * 16);
-    // Consume every fragment here, so the wait for these loads happens once, before the key
-    // loop: otherwise the loop's MFMAs carry waits that also drain the tile prefetch.
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks) asm volatile("" : "+v"(qf[ks]));
-    const uint16_t* qp = a.q_pe + qrow * kDRope + g * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      *reinterpret_cast<bf16x8*>(smem + kQpeOff + wave * 4096 + ks * 1024 + lane * 16) =
-          *reinterpret_cast<const bf16x8*>(qp + ks * 16);
-  }
 
   // Staging of this stream's cache rows.  A latent row is one wave instruction (64 lanes x
   // 16 B); the rotary instruction of wave w moves 16-byte chunks 2w, 2w + 1 of all 32 rows
@@ -301,6 +291,14 @@ verify_attn_kernel(VerifyArgs a) {
   const int t_begin = sp * a.tiles_per_split[grp];
   const int t_end = min((L + kTileKeys - 1) / kTileKeys, t_begin + a.tiles_per_split[grp]);
   const int t_mask = max(t_begin, min(t_end, P / kTileKeys));  // first tile holding tree keys
+
+  // Q^T fragments of this wave's head block: lane holds head `head`, dims 16 ks + 8 g .. +7.
+  // The 32 latent k-steps stay in VGPRs for the whole key range; the 4 rotary k-steps are
+  // staged once into LDS (the register file is full: O^T alone takes all 256 AGPRs).  They are
+  // loaded in the first pass, right behind the first tile's staging, so that one wait covers
+  // both.
+  bf16x8 qf[32];
+
 
   // ---- S^T of a tile held in stage stg: 32 latent + 4 rotary k-steps
   auto score_mma = [&](int stg, auto&& hook, auto&& dma) __attribute__((always_inline)) -> f32x16 {
@@ -482,6 +480,21 @@ verify_attn_kernel(VerifyArgs a) {
     mx_run = -INFINITY;
 
     stage_tile(t_begin, 0);
+    if (attempt == 0) {
+      const size_t qrow = ((size_t)s * Q + qc) * kHeads + head;
+      const uint16_t* ql = a.q_lat + qrow * kDLat + g * 8;
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(ql + ks * 16);
+      // Consume every fragment here, so the wait for these loads happens once, before the key
+      // loop: otherwise the loop's MFMAs carry waits that also drain the tile prefetch.
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) asm volatile("" : "+v"(qf[ks]));
+      const uint16_t* qp = a.q_pe + qrow * kDRope + g * 8;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        *reinterpret_cast<bf16x8*>(smem + kQpeOff + wave * 4096 + ks * 1024 + lane * 16) =
+            *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+    }
     int t = t_begin;
     // first tile: sets the reference max on the first pass, no value product yet
     if (attempt == 0) {
