@@ -74,6 +74,9 @@ constexpr int kPBytes = 4 * 2 * 64 * 16;                  // 8 KiB per buffer
 constexpr int kPOff = kStages * kStageBytes;
 constexpr int kQpeOff = kPOff + 2 * kPBytes;
 constexpr int kSmemBytes = kQpeOff + 4 * 4 * 64 * 16;     // 144896 B
+// Output transpose area of a wave at the end: 32 rows x (128 fp32 + 16 B pad), inside the stages.
+constexpr int kTRow = 128 * 4 + 16;
+static_assert(4 * 32 * kTRow <= kPOff, "the output transpose areas must not reach the P buffers");
 // Scores are exponentiated against a per-head reference max taken from the first 32 keys.
 // If the true max ends above ref + kRefHi or below ref - kRefLo (log2 units) the workgroup
 // repeats its key range once with the exact max as reference.  Inside the window every
@@ -545,26 +548,41 @@ verify_attn_kernel(VerifyArgs a) {
       a.part_lse[grp][(size_t)sp * part_rows + part_row(wave >> 1, head)] = lse_v;
   }
   __syncthreads();
+  // Output, one head block at a time through this wave's own LDS area (the key stages are free
+  // after the last barrier): the accumulator holds 16-byte runs of 32 rows, the read back hands
+  // each lane one 16-byte chunk of a row, so that each store writes two rows' 512-byte segments
+  // (this wave's 128 dims) instead of 32-byte pieces of 32 rows.
+  unsigned char* tbuf = smem + wave * (32 * kTRow);
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
     if ((hb >> 1) >= n_nodes) continue;
-    const float lh = l_sh[hb * 32 + c32];
-    const float inv = (lh > 0.f ? 1.0f / lh : 0.f) + poison;
-    const int h = (hb & 1) * 32 + c32;
-    float* dst = n_split == 1 ? a.out + (((size_t)s * Q + q0 + (hb >> 1)) * kHeads + h) * kDLat
-                              : a.part_out[grp] + ((size_t)sp * part_rows + part_row(hb >> 1, h)) * kDLat;
-    dst += wave * 128 + 4 * g;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         float4 v;
-        v.x = o[hb][db][4 * i4 + 0] * inv;
-        v.y = o[hb][db][4 * i4 + 1] * inv;
-        v.z = o[hb][db][4 * i4 + 2] * inv;
-        v.w = o[hb][db][4 * i4 + 3] * inv;
-        *reinterpret_cast<float4*>(dst + 32 * db + 8 * i4) = v;
+        v.x = o[hb][db][4 * i4 + 0];
+        v.y = o[hb][db][4 * i4 + 1];
+        v.z = o[hb][db][4 * i4 + 2];
+        v.w = o[hb][db][4 * i4 + 3];
+        *reinterpret_cast<float4*>(tbuf + c32 * kTRow + (32 * db + 8 * i4 + 4 * g) * 4) = v;
       }
+    }
+    const int h0 = (hb & 1) * 32;
+    float* dst = n_split == 1 ? a.out + (((size_t)s * Q + q0 + (hb >> 1)) * kHeads + h0) * kDLat
+                              : a.part_out[grp] + ((size_t)sp * part_rows + part_row(hb >> 1, h0)) * kDLat;
+    dst += wave * 128 + (lane & 31) * 4;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 2 * j + (lane >> 5);
+      const float lh = l_sh[hb * 32 + r];
+      const float inv = (lh > 0.f ? 1.0f / lh : 0.f) + poison;
+      float4 v = *reinterpret_cast<const float4*>(tbuf + r * kTRow + (lane & 31) * 16);
+      v.x *= inv;
+      v.y *= inv;
+      v.z *= inv;
+      v.w *= inv;
+      *reinterpret_cast<float4*>(dst + (size_t)r * kDLat) = v;
     }
   }
 }
