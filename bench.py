@@ -268,6 +268,34 @@ def summarize_pmc(fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_d
     return "\n".join(lines) + "\n"
 
 
+def summarize_counters(db: str, command: str) -> str:
+    """Mean per verify launch of every counter in a ``rocprofv3 --pmc`` database, plus the MFMA
+    utilisation (busy cycles of the matrix units over active cycles, per SIMD) and the MFMA
+    FLOPs these counters imply."""
+    rows = _db_rows(db, "select name, dispatch_id, counter_name, counter_value from pmc_events")
+    tot = {}  # (counter, dispatch) -> sum over the counter's hardware instances
+    for name, disp, cn, v in rows:
+        if "verify_attn_kernel" in name:
+            tot[(cn, disp)] = tot.get((cn, disp), 0.0) + v
+    if not tot:
+        raise SystemExit(f"no verify_attn_kernel samples in {db}")
+    per = {}
+    for (cn, _), v in tot.items():
+        per.setdefault(cn, []).append(v)
+    mean = {k: sum(v) / len(v) for k, v in per.items()}
+    lines = [f"command: {command}", f"kernel_source_sha256: {kernel_sha()}",
+             "counter means per verify_attn_kernel dispatch (hardware instances summed):"]
+    lines += [f"  {k}: {mean[k]:.6g}  (dispatches: {len(per[k])})" for k in sorted(mean)]
+    if "MfmaUtil" in mean:
+        lines.append(f"mfma_busy_pct: {mean['MfmaUtil']:.2f}")
+    if "MfmaFlopsBF16" in mean:
+        lines.append(f"mfma_bf16_flop_per_launch: {mean['MfmaFlopsBF16']:.6g}")
+    if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_LDS_IDX_ACTIVE" in mean and mean["SQ_LDS_IDX_ACTIVE"]:
+        lines.append(f"lds_bank_conflict_cycles_per_active_cycle: "
+                     f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_LDS_IDX_ACTIVE']:.4f}")
+    return "\n".join(lines) + "\n"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +309,8 @@ def main() -> int:
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DB", "COMMAND", "SKIP"),
                     help="print a per-kernel summary of a rocprofv3 kernel-trace database and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("DB", "COMMAND"),
+                    help="print the verify launch's mean counters (MFMA utilisation, LDS) and exit")
     ap.add_argument("--summarize-pmc", nargs=6,
                     metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB", "COPY_BYTES", "COMMANDS"),
                     help="print HBM bytes per verify launch from FETCH_SIZE / WRITE_SIZE runs and exit")
@@ -288,6 +318,9 @@ def main() -> int:
     if args.summarize_trace:
         db, cmd, skip = args.summarize_trace
         print(summarize_trace(db, cmd, int(skip)), end="")
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters), end="")
         return 0
     if args.summarize_pmc:
         f, w, cf, cw, nbytes, cmds = args.summarize_pmc
