@@ -195,6 +195,37 @@ def layers_table(lib, dev, w, parents, draft_tok, target_tok, keep_bits, n_keep_
             "moved_bytes": moved_bytes, "gbs": round(moved_bytes / (fused * 1e-6) / 1e9, 1)}
 
 
+def workloads_table(lib, dev, skip: str):
+    """``ddtree_verify_attn_ex`` (automatic split plan) us/call, TFLOP/s and % of the bf16 peak on
+    every named workload but ``skip``: 100 calls in one HIP graph, best of 5 replays."""
+    import torch
+    import synth
+    table = {}
+    for name, w in synth.WORKLOADS.items():
+        if name == skip:
+            continue
+        b = synth.make_batch(w, with_path=False)
+
+        def up(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        ql, qp, ckv, kpe = up(b.q_lat), up(b.q_pe), up(b.ckv), up(b.kpe)
+        par = torch.from_numpy(b.parents).to(dev)
+        out = torch.empty((w.streams, w.q_len, w.heads, 512), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.streams, w.q_len, w.heads), dtype=torch.float32, device=dev)
+        nbytes = lib.workspace_size(w.prefix, w.q_len, w.streams, 0)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
+        us = time_calls(lambda: lib.verify_attn_ex(ql, qp, ckv, kpe, w.prefix, par, out=out, lse=lse, workspace=ws))
+        flops = 2.0 * w.heads * (576 + 512) * visible_pairs(b.parents, w.prefix)
+        tf = flops / (us * 1e-6) / 1e12
+        table[name] = {"us_per_call": round(us, 2), "tflops": round(tf, 2),
+                       "pct_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                       "splits": lib.num_splits(w.prefix, w.q_len, w.streams, 0)}
+        del ql, qp, ckv, kpe, out, lse, ws
+    torch.cuda.empty_cache()
+    return table
+
+
 def append_table(lib, dev, w, parents):
     """``ddtree_append_tree_kv`` us/call on the workload's trees: the projection's fp32 rows in,
     the bf16 cache rows out, at the workload's prefix (tables cover the positions)."""
@@ -406,6 +437,7 @@ def main() -> int:
     compact_us = time_calls(lambda: _lib.compact_kv(ckv, kpe, w.prefix, keep, n_keep))
     layers = layers_table(_lib, dev, w, parents, draft_tok, target_tok, b.keep, b.n_keep)
     append = append_table(_lib, dev, w, parents)
+    others = workloads_table(_lib, dev, w.name)
 
     flops = 2.0 * w.heads * (576 + 512) * visible_pairs(b.parents, w.prefix)
     tflops_step = flops / (ms_step * 1e-3) / 1e12
@@ -437,6 +469,7 @@ def main() -> int:
                    "tree_build_us_per_call": build_us,
                    "accept_compact_layers": layers,
                    "append_tree_kv": append,
+                   "verify_other_workloads": others,
                    "verify_tflops": round(achieved, 2),
                    "pct_mfma_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
                    "algorithmic_bytes": algorithmic_bytes(w, w.streams),

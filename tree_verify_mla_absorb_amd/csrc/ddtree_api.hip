@@ -68,25 +68,27 @@ void set_splits(Plan& p, int g, int want) {
 }
 
 // Estimated time of a plan, in units of one workgroup-tile (32 keys x 128 query-heads, about
-// 9 MFLOP, ~1-1.5 us on one CU).  Workgroups of group 0 are dispatched first, then group 1's,
-// each to the next free CU.  When group 0 fills whole rounds, group 1 runs in rounds of its own
-// after it; otherwise the estimate is the larger of group 0's own rounds and the
-// list-scheduling bound (total work / CUs + one group-1 workgroup).  A split group pays for its
-// partials: 2 KiB per row written and read back by the merge (~0.06 tile-times per 128 rows of
-// one split on the whole GPU's bandwidth) plus a fixed cost for the merge launch.
+// 9 MFLOP, ~1-1.5 us on one CU).  When every workgroup fits on the CUs at once, the longest one
+// decides.  Otherwise, when group 0 fills whole rounds, group 1 adds rounds of its own; else the
+// estimate is the larger of group 0's own rounds and the list-scheduling bound (total work /
+// CUs + one group-1 workgroup).  A split group pays for its partials: 2 KiB per row written and
+// read back by the merge (~0.06 tile-times per 128 rows of one split on the whole GPU's
+// bandwidth) plus about 3 tile-times for the merge launch (measured: a merge costs ~3 us).
 double plan_cost(const Plan& p, long long units0, long long units1, int cus) {
   const double c0 = p.tiles_per_split[0], c1 = p.tiles_per_split[1];
   const long long n0 = units0 * p.splits[0], n1 = units1 * p.splits[1];
   const double end0 = n0 ? (double)((n0 + cus - 1) / cus) * c0 : 0.0;
   double t = end0;
-  if (n1) {
+  if (n0 + n1 <= cus) {
+    t = fmax(n0 ? c0 : 0.0, n1 ? c1 : 0.0);
+  } else if (n1) {
     if (n0 % cus == 0)
       t = end0 + (double)((n1 + cus - 1) / cus) * c1;
     else
       t = fmax(end0, ((double)n0 * c0 + (double)n1 * c1) / cus + c1);
   }
-  if (n0 && p.splits[0] > 1) t += 0.06 * (double)n0 + 1.0;
-  if (n1 && p.splits[1] > 1) t += 0.03 * (double)n1 + 1.0;
+  if (n0 && p.splits[0] > 1) t += 0.06 * (double)n0 + 3.0;
+  if (n1 && p.splits[1] > 1) t += 0.03 * (double)n1 + 3.0;
   return t;
 }
 

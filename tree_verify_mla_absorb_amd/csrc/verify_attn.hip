@@ -588,7 +588,12 @@ verify_attn_kernel(VerifyArgs a) {
 }
 
 // Merge of key-range splits by log-sum-exp: lse = log sum_k exp(lse_k),
-// out = sum_k exp(lse_k - lse) out_k.  One thread per (partial row, 4 dims).
+// out = sum_k exp(lse_k - lse) out_k.  One thread per (partial row, 4 dims).  The splits are
+// read in chunks of kMergeChunk with every load of a chunk in flight, and merged online: the
+// running sums are rescaled when a chunk raises the running max.  (A loop with one split per
+// iteration waits out a full memory latency per split, which dominated at tens of splits.)
+constexpr int kMergeChunk = 8;
+
 __global__ void __launch_bounds__(256) verify_combine_kernel(CombineArgs a) {
   const int tid = blockIdx.x * blockDim.x + threadIdx.x;
   const int row = tid >> 7;
@@ -605,27 +610,53 @@ __global__ void __launch_bounds__(256) verify_combine_kernel(CombineArgs a) {
   } else {
     orow = ((row >> 6) * a.q_len + a.q_len - 1) * kHeads + (row & (kHeads - 1));
   }
-  float mx = -INFINITY;
-  for (int k = 0; k < a.n_splits; ++k) mx = fmaxf(mx, a.part_lse[(size_t)k * a.rows + row]);
-  float den = 0.f;
+  float mx = -INFINITY, den = 0.f;
+  float poison = 0.f;  // NaN once any split is NaN (a poisoned stream), whatever the others hold
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k = 0; k < a.n_splits; ++k) {
-    const float lk = a.part_lse[(size_t)k * a.rows + row];
-    const float w = lk == -INFINITY ? 0.f : expf(lk - mx);
-    den += w;
-    const float4 v = *reinterpret_cast<const float4*>(a.part_out + ((size_t)k * a.rows + row) * kDLat + 4 * c4);
-    acc.x += w * v.x;
-    acc.y += w * v.y;
-    acc.z += w * v.z;
-    acc.w += w * v.w;
+  for (int k0 = 0; k0 < a.n_splits; k0 += kMergeChunk) {
+    float lk[kMergeChunk];
+    float4 v[kMergeChunk];
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) {
+      const int k = k0 + j;
+      lk[j] = -INFINITY;
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < a.n_splits) {
+        lk[j] = a.part_lse[(size_t)k * a.rows + row];
+        v[j] = *reinterpret_cast<const float4*>(a.part_out + ((size_t)k * a.rows + row) * kDLat + 4 * c4);
+      }
+    }
+    float cmx = mx;
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) {
+      cmx = fmaxf(cmx, lk[j]);
+      if (lk[j] != lk[j]) poison = lk[j];
+    }
+    if (cmx == -INFINITY) continue;  // nothing but empty splits so far
+    const float r = mx == -INFINITY ? 0.f : expf(mx - cmx);
+    den *= r;
+    acc.x *= r;
+    acc.y *= r;
+    acc.z *= r;
+    acc.w *= r;
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) {
+      const float w = lk[j] == -INFINITY ? 0.f : expf(lk[j] - cmx);
+      den += w;
+      acc.x += w * v[j].x;
+      acc.y += w * v[j].y;
+      acc.z += w * v[j].z;
+      acc.w += w * v[j].w;
+    }
+    mx = cmx;
   }
-  const float inv = 1.0f / den;
+  const float inv = 1.0f / den + poison;
   acc.x *= inv;
   acc.y *= inv;
   acc.z *= inv;
   acc.w *= inv;
   *reinterpret_cast<float4*>(a.out + (size_t)orow * kDLat + 4 * c4) = acc;
-  if (c4 == 0) a.lse[orow] = mx + logf(den);
+  if (c4 == 0) a.lse[orow] = mx + logf(den) + poison;
 }
 
 }  // namespace
