@@ -72,7 +72,8 @@ extern "C" {
 
 /* Bits of the optional device status word. */
 #define DDTREE_STATUS_BAD_PARENTS 1 /* a parents[] entry is not an earlier node; that node's
-                                       ancestor walk stops there                               */
+                                       ancestor chain stops there (attention), the stream is
+                                       skipped (acceptance, tree rows)                         */
 #define DDTREE_STATUS_BAD_KEEP 2    /* keep[]/n_keep of a stream invalid; that stream untouched */
 #define DDTREE_STATUS_BAD_PREFIX 4  /* a per-stream prefix length out of range; see the ragged calls */
 #define DDTREE_STATUS_BAD_POSITION 8 /* a tree position past the rotary tables; see ddtree_append_tree_kv */

@@ -23,9 +23,10 @@
 //
 // Workgroup = 4 waves over 2 tree nodes x 64 heads = 4 head blocks of 32 query-heads.  For the
 // scores, wave w owns head block w: node (first + w / 2), heads 32 (w & 1) .. +31, so the tree
-// mask is wave-uniform -- one 64-bit ancestor-or-self mask walked from parents[] with a walk
-// bounded by q_len (the bounded-walk lesson of "The Microsecond Verdict", section "The Crash
-// That Demanded a Fix").  For the value product the waves split the 512 latent dims instead
+// mask is wave-uniform -- one 64-bit ancestor-or-self mask, built from one load of parents[]
+// by a fixed number of pointer-jumping steps, so no input can make it run long (the bounded-
+// walk lesson of "The Microsecond Verdict", section "The Crash That Demanded a Fix").  For the
+// value product the waves split the 512 latent dims instead
 // (wave w: dims 128 w .. +127 of all four head blocks) and share the probabilities through
 // LDS, so each V^T fragment read feeds four MFMAs.
 //
