@@ -55,7 +55,11 @@ def test_small_shapes_no_split(lib, s, p, q):
 
 
 @pytest.mark.parametrize("s,p,q,splits", [(1, 300, 9, 2), (2, 300, 33, 5), (1, 1000, 64, 16), (1, 64, 64, 2),
-                                          (3, 129, 5, 3), (1, 4000, 33, 0)])
+                                          (3, 129, 5, 3), (1, 4000, 33, 0),
+                                          # odd-node workgroups dispatched partly ahead of the
+                                          # pairs: 25 of them (5 splits of 2 tiles; 8 first),
+                                          # and 24 (8 first)
+                                          (5, 300, 9, 7), (24, 40, 3, 1)])
 def test_forced_and_auto_splits(lib, s, p, q, splits):
     b = synth.random_inputs(2000 + p + q, s, p, q)
     check(lib, b, p, splits=splits, what=f"split {s},{p},{q}/{splits}")
