@@ -335,6 +335,9 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail-tables", action="store_true",
+                    help="skip the per-call tables of the other entry points and workloads (for profiler "
+                         "runs that must see only the step's own launches)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 3 times (for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -429,15 +432,20 @@ def main() -> int:
     ms_step = start.elapsed_time(end) / args.steps
     verify_ms = float(np.mean([a.elapsed_time(bb) for a, bb in evs]))
 
-    # per-call times of the acceptance and compaction entry points (outside the timed steps)
-    accept_us = accept_table(_lib, dev)
-    build_us = build_table(_lib, dev)
-    fused_us = time_calls(lambda: _lib.accept_compact(ckv, kpe, w.prefix, parents, draft_tok, target_tok, keep=keep,
-                                                      n_keep=n_keep, next_token=next_tok))
-    compact_us = time_calls(lambda: _lib.compact_kv(ckv, kpe, w.prefix, keep, n_keep))
-    layers = layers_table(_lib, dev, w, parents, draft_tok, target_tok, b.keep, b.n_keep)
-    append = append_table(_lib, dev, w, parents)
-    others = workloads_table(_lib, dev, w.name)
+    # per-call times of the other entry points and workloads (outside the timed steps)
+    tables = {}
+    if not args.no_detail_tables:
+        fused_us = time_calls(lambda: _lib.accept_compact(ckv, kpe, w.prefix, parents, draft_tok, target_tok,
+                                                          keep=keep, n_keep=n_keep, next_token=next_tok))
+        tables = {
+            "accept_compact_us_per_call": round(fused_us, 2),
+            "compact_kv_us_per_call": round(time_calls(lambda: _lib.compact_kv(ckv, kpe, w.prefix, keep, n_keep)), 2),
+            "tree_accept_us_per_call": accept_table(_lib, dev),
+            "tree_build_us_per_call": build_table(_lib, dev),
+            "accept_compact_layers": layers_table(_lib, dev, w, parents, draft_tok, target_tok, b.keep, b.n_keep),
+            "append_tree_kv": append_table(_lib, dev, w, parents),
+            "verify_other_workloads": workloads_table(_lib, dev, w.name),
+        }
 
     flops = 2.0 * w.heads * (576 + 512) * visible_pairs(b.parents, w.prefix)
     tflops_step = flops / (ms_step * 1e-3) / 1e12
@@ -463,13 +471,7 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "detail": {"verify_us_per_call": round(verify_ms * 1e3, 2),
                    "accept_compact_us_per_call_incl_gap": round((ms_step - verify_ms) * 1e3, 2),
-                   "accept_compact_us_per_call": round(fused_us, 2),
-                   "compact_kv_us_per_call": round(compact_us, 2),
-                   "tree_accept_us_per_call": accept_us,
-                   "tree_build_us_per_call": build_us,
-                   "accept_compact_layers": layers,
-                   "append_tree_kv": append,
-                   "verify_other_workloads": others,
+                   **tables,
                    "verify_tflops": round(achieved, 2),
                    "pct_mfma_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
                    "algorithmic_bytes": algorithmic_bytes(w, w.streams),
