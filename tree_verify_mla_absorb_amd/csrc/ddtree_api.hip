@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/ddtree.h"
 #include "kernels.h"
 
@@ -492,12 +494,13 @@ int check_layers(const ddtree_kv_cache* caches, int n_layers, const Range* small
     a->ckv[l] = static_cast<uint16_t*>(c.ckv);
     a->kpe[l] = static_cast<uint16_t*>(c.kpe);
   }
-  for (int i = 0; i < 2 * n_layers; ++i) {
-    for (int j = i + 1; j < 2 * n_layers; ++j)
-      if (overlap(r[i], r[j])) return DDTREE_ERR_ALIAS;
+  // No two caches overlap: sorted by start, each range must end before the next one starts.
+  std::sort(r, r + 2 * n_layers, [](const Range& x, const Range& y) { return x.lo < y.lo; });
+  for (int i = 0; i + 1 < 2 * n_layers; ++i)
+    if (overlap(r[i], r[i + 1])) return DDTREE_ERR_ALIAS;
+  for (int i = 0; i < 2 * n_layers; ++i)
     for (int k = 0; k < n_small; ++k)
       if (overlap(r[i], small[k])) return DDTREE_ERR_ALIAS;
-  }
   a->kv_rows = kv_rows;
   a->n_streams = n_streams;
   a->n_layers = n_layers;
