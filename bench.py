@@ -226,6 +226,28 @@ def workloads_table(lib, dev, skip: str):
     return table
 
 
+def ragged_table(lib, dev, w, q_lat, q_pe, ckv, kpe, parents_bits):
+    """``ddtree_verify_attn_ragged`` on the workload's inputs with per-stream prefixes drawn
+    uniformly from [prefix / 4, prefix] (a batch after some steps of compaction): us/call and
+    TFLOP/s over each stream's own visible keys, next to the uniform-prefix call."""
+    import torch
+    import synth
+    rng = synth.rng_for(w.seed, 0, 99)
+    prefixes = rng.integers(w.prefix // 4, w.prefix + 1, size=w.streams).astype(np.int32)
+    pl = torch.from_numpy(prefixes).to(dev)
+    par = torch.from_numpy(parents_bits).to(dev)
+    out = torch.empty((w.streams, w.q_len, w.heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.streams, w.q_len, w.heads), dtype=torch.float32, device=dev)
+    nbytes = lib.workspace_size(w.prefix, w.q_len, w.streams, 0)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
+    us = time_calls(lambda: lib.verify_attn_ragged(q_lat, q_pe, ckv, kpe, pl, w.prefix, par, out=out, lse=lse,
+                                                   workspace=ws), n=20, replays=3)
+    flops = sum(2.0 * w.heads * (576 + 512) * visible_pairs(parents_bits[s:s + 1], int(prefixes[s]))
+                for s in range(w.streams))
+    return {"prefixes": f"uniform in [{w.prefix // 4}, {w.prefix}], mean {prefixes.mean():.0f}",
+            "us_per_call": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 2)}
+
+
 def append_table(lib, dev, w, parents):
     """``ddtree_append_tree_kv`` us/call on the workload's trees: the projection's fp32 rows in,
     the bf16 cache rows out, at the workload's prefix (tables cover the positions)."""
@@ -445,6 +467,7 @@ def main() -> int:
             "accept_compact_layers": layers_table(_lib, dev, w, parents, draft_tok, target_tok, b.keep, b.n_keep),
             "append_tree_kv": append_table(_lib, dev, w, parents),
             "verify_other_workloads": workloads_table(_lib, dev, w.name),
+            "verify_ragged": ragged_table(_lib, dev, w, q_lat, q_pe, ckv, kpe, b.parents),
         }
 
     flops = 2.0 * w.heads * (576 + 512) * visible_pairs(b.parents, w.prefix)
