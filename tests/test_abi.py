@@ -269,3 +269,16 @@ def test_append_argument_errors():
     assert append(kv=G + 0x10000000 + 64) == _lib.ERR_ALIAS   # kv inside the rotary cache
     assert append(cos=G + 1024) == _lib.ERR_ALIAS              # table inside the latent cache
     assert append(status=B + 16) == _lib.ERR_ALIAS             # status word inside kv
+
+
+def test_automatic_split_plan_on_the_five_workloads():
+    """The plan the library picks for each seeded workload on a 256-CU part (the count it assumes
+    when no device answers).  These are the plans measured best, or within 2% of the best, in a
+    sweep of forced split counts on the GPU; the reported count is the larger group's."""
+    assert _lib.num_splits(256, 9, 1, 0) == 1        # one stream, 9 tiles: no merge pays off
+    assert _lib.num_splits(1024, 33, 8, 0) == 1      # 136 workgroups fit at once: no split
+    assert _lib.num_splits(1024, 9, 64, 0) == 4      # the odd node split 4 ways, pairs whole
+    assert _lib.num_splits(4096, 33, 1, 0) == 15     # one long stream: 15 splits of 9 tiles
+    assert _lib.num_splits(4096, 33, 64, 0) == 4     # 1024 pair workgroups = 4 rounds; odd node x4
+    assert _lib.workspace_size(1024, 33, 8, 0) == 0  # unsplit: no workspace
+    assert _lib.workspace_size(4096, 33, 64, 0) > 0
