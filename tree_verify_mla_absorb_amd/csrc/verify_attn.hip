@@ -383,12 +383,18 @@ verify_attn_kernel(VerifyArgs a) {
   auto pfrag = [&](int pbuf, int hb, int slice) __attribute__((always_inline)) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(smem + kPOff + pbuf * kPBytes + hb * 2048 + slice * 1024 + lane16);
   };
-  auto value_prologue = [&](int stg, int pbuf, bf16x8 (&p0)[4], bf16x8& vf) __attribute__((always_inline)) {
+  // kHalf: a workgroup of one node (group 1), whose head blocks 2 and 3 only repeat 0 and 1 --
+  // their value product is skipped (their outputs are never written).
+  auto value_prologue = [&](int stg, int pbuf, bf16x8 (&p0)[4], bf16x8& vf, auto half_tag)
+                            __attribute__((always_inline)) {
+    constexpr int kNhb = decltype(half_tag)::value ? 2 : 4;
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) p0[hb] = pfrag(pbuf, hb, 0);
+    for (int hb = 0; hb < kNhb; ++hb) p0[hb] = pfrag(pbuf, hb, 0);
     vf = vfrag(stg, 0);
   };
-  auto values = [&](int stg, int pbuf, bf16x8 (&p0)[4], bf16x8& vf, auto&& side) __attribute__((always_inline)) {
+  auto values = [&](int stg, int pbuf, bf16x8 (&p0)[4], bf16x8& vf, auto&& side, auto half_tag)
+                    __attribute__((always_inline)) {
+    constexpr int kNhb = decltype(half_tag)::value ? 2 : 4;
     bf16x8 p1[4];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -396,10 +402,10 @@ verify_attn_kernel(VerifyArgs a) {
       if (k + 1 < 8) vf = vfrag(stg, k + 1);
       if (k == kP1Step) {
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) p1[hb] = pfrag(pbuf, hb, 1);
+        for (int hb = 0; hb < kNhb; ++hb) p1[hb] = pfrag(pbuf, hb, 1);
       }
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb)
+      for (int hb = 0; hb < kNhb; ++hb)
         o[hb][k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, k < 4 ? p0[hb] : p1[hb], o[hb][k & 3], 0, 0, 0);
       side(k);
       __builtin_amdgcn_sched_barrier(0);
@@ -413,7 +419,8 @@ verify_attn_kernel(VerifyArgs a) {
   //      A steady step runs the value product of tile t - 1 with the softmax of tile t spread
   //      between its MFMAs.  The first step of a pass has no previous tile; on the first pass it
   //      also sets the reference max from this tile before any exponential.
-  auto step = [&](int t, auto masked_tag, auto first_tag, auto set_ref_tag) __attribute__((always_inline)) {
+  auto step = [&](int t, auto masked_tag, auto first_tag, auto set_ref_tag, auto half_tag)
+                  __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first_tag)::value;
     constexpr bool kSetRef = decltype(set_ref_tag)::value;
     constexpr bool kMasked = decltype(masked_tag)::value;
@@ -434,7 +441,8 @@ verify_attn_kernel(VerifyArgs a) {
       st = score_mma(stg, no_hook, dma);
     }
     else
-      st = score_mma(stg, [&]() __attribute__((always_inline)) { value_prologue(prev_stg, prev_pbuf, p0, vf); }, dma);
+      st = score_mma(
+          stg, [&]() __attribute__((always_inline)) { value_prologue(prev_stg, prev_pbuf, p0, vf, half_tag); }, dma);
     bf16x8 pb[2];
     float psum = 0.f, mx = -INFINITY;
     if constexpr (kFirst) {
@@ -459,11 +467,14 @@ verify_attn_kernel(VerifyArgs a) {
       publish(pbuf, 0, pb[0]);
       publish(pbuf, 1, pb[1]);
     } else {
-      values(prev_stg, prev_pbuf, p0, vf, [&](int k) __attribute__((always_inline)) {
-        if (k < kStageInstrs - kDmaInScores) dma(kDmaInScores + k);
-        prob_pair(st, t, k, masked_tag, pb, psum, mx);
-        if ((k & 3) == 3) publish(pbuf, k >> 2, pb[k >> 2]);
-      });
+      values(
+          prev_stg, prev_pbuf, p0, vf,
+          [&](int k) __attribute__((always_inline)) {
+            if (k < kStageInstrs - kDmaInScores) dma(kDmaInScores + k);
+            prob_pair(st, t, k, masked_tag, pb, psum, mx);
+            if ((k & 3) == 3) publish(pbuf, k >> 2, pb[k >> 2]);
+          },
+          half_tag);
     }
     l_run += psum;
     mx_run = fmaxf(mx_run, mx * cs);
@@ -473,67 +484,75 @@ verify_attn_kernel(VerifyArgs a) {
   for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[hb][db] = f32x16{};
-  for (int attempt = 0; attempt < 2 && t_begin < t_end; ++attempt) {
-    if (attempt > 0) {
+  // The key passes, instantiated separately for the one-node workgroups of group 1.
+  auto passes = [&](auto half_tag) __attribute__((always_inline)) {
+    for (int attempt = 0; attempt < 2 && t_begin < t_end; ++attempt) {
+      if (attempt > 0) {
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb)
+        for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) o[hb][db] = f32x16{};
-    }
-    l_run = 0.f;
-    mx_run = -INFINITY;
+          for (int db = 0; db < 4; ++db) o[hb][db] = f32x16{};
+      }
+      l_run = 0.f;
+      mx_run = -INFINITY;
 
-    stage_tile(t_begin, 0);
-    if (attempt == 0) {
-      const size_t qrow = ((size_t)s * Q + qc) * kHeads + head;
-      const uint16_t* ql = a.q_lat + qrow * kDLat + g * 8;
+      stage_tile(t_begin, 0);
+      if (attempt == 0) {
+        const size_t qrow = ((size_t)s * Q + qc) * kHeads + head;
+        const uint16_t* ql = a.q_lat + qrow * kDLat + g * 8;
 #pragma unroll
-      for (int ks = 0; ks < 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(ql + ks * 16);
-      // Consume every fragment here, so the wait for these loads happens once, before the key
-      // loop: otherwise the loop's MFMAs carry waits that also drain the tile prefetch.
+        for (int ks = 0; ks < 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(ql + ks * 16);
+        // Consume every fragment here, so the wait for these loads happens once, before the key
+        // loop: otherwise the loop's MFMAs carry waits that also drain the tile prefetch.
 #pragma unroll
-      for (int ks = 0; ks < 32; ++ks) asm volatile("" : "+v"(qf[ks]));
-      const uint16_t* qp = a.q_pe + qrow * kDRope + g * 8;
+        for (int ks = 0; ks < 32; ++ks) asm volatile("" : "+v"(qf[ks]));
+        const uint16_t* qp = a.q_pe + qrow * kDRope + g * 8;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        *reinterpret_cast<bf16x8*>(smem + kQpeOff + wave * 4096 + ks * 1024 + lane * 16) =
-            *reinterpret_cast<const bf16x8*>(qp + ks * 16);
-    }
-    int t = t_begin;
-    // first tile: sets the reference max on the first pass, no value product yet
-    if (attempt == 0) {
-      if (t < t_mask)
-        step(t, Flag<false>{}, Flag<true>{}, Flag<true>{});
-      else
-        step(t, Flag<true>{}, Flag<true>{}, Flag<true>{});
-    } else {  // the second pass keeps the exact max found by the first
-      if (t < t_mask)
-        step(t, Flag<false>{}, Flag<true>{}, Flag<false>{});
-      else
-        step(t, Flag<true>{}, Flag<true>{}, Flag<false>{});
-    }
-    ++t;
-    for (; t < t_mask; ++t) step(t, Flag<false>{}, Flag<false>{}, Flag<false>{});
-    for (; t < t_end; ++t) step(t, Flag<true>{}, Flag<false>{}, Flag<false>{});
-    // last tile's values
-    __syncthreads();
-    {
-      const int last_stg = (t_end - 1 - t_begin) % kStages, last_pbuf = (t_end - 1 - t_begin) & 1;
-      bf16x8 p0[4], vf;
-      value_prologue(last_stg, last_pbuf, p0, vf);
-      values(last_stg, last_pbuf, p0, vf, no_side);
+        for (int ks = 0; ks < 4; ++ks)
+          *reinterpret_cast<bf16x8*>(smem + kQpeOff + wave * 4096 + ks * 1024 + lane * 16) =
+              *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+      }
+      int t = t_begin;
+      // first tile: sets the reference max on the first pass, no value product yet
+      if (attempt == 0) {
+        if (t < t_mask)
+          step(t, Flag<false>{}, Flag<true>{}, Flag<true>{}, half_tag);
+        else
+          step(t, Flag<true>{}, Flag<true>{}, Flag<true>{}, half_tag);
+      } else {  // the second pass keeps the exact max found by the first
+        if (t < t_mask)
+          step(t, Flag<false>{}, Flag<true>{}, Flag<false>{}, half_tag);
+        else
+          step(t, Flag<true>{}, Flag<true>{}, Flag<false>{}, half_tag);
+      }
+      ++t;
+      for (; t < t_mask; ++t) step(t, Flag<false>{}, Flag<false>{}, Flag<false>{}, half_tag);
+      for (; t < t_end; ++t) step(t, Flag<true>{}, Flag<false>{}, Flag<false>{}, half_tag);
+      // last tile's values
+      __syncthreads();
+      {
+        const int last_stg = (t_end - 1 - t_begin) % kStages, last_pbuf = (t_end - 1 - t_begin) & 1;
+        bf16x8 p0[4], vf;
+        value_prologue(last_stg, last_pbuf, p0, vf, half_tag);
+        values(last_stg, last_pbuf, p0, vf, no_side, half_tag);
+      }
+
+      // Was the reference max a safe choice for every head of the workgroup?
+      const float mfull = half_max(mx_run);
+      const bool redo = mfull != -INFINITY && (mfull > m_ref + kRefHi || mfull < m_ref - kRefLo);
+      if (threadIdx.x == 0) redo_s = 0;
+      __syncthreads();
+      if (attempt == 0 && __builtin_amdgcn_ballot_w64(redo) != 0 && lane == 0) redo_s = 1;
+      __syncthreads();
+      if (redo_s == 0) break;
+      m_ref = mfull == -INFINITY ? 0.f : mfull;
     }
 
-    // Was the reference max a safe choice for every head of the workgroup?
-    const float mfull = half_max(mx_run);
-    const bool redo = mfull != -INFINITY && (mfull > m_ref + kRefHi || mfull < m_ref - kRefLo);
-    if (threadIdx.x == 0) redo_s = 0;
-    __syncthreads();
-    if (attempt == 0 && __builtin_amdgcn_ballot_w64(redo) != 0 && lane == 0) redo_s = 1;
-    __syncthreads();
-    if (redo_s == 0) break;
-    m_ref = mfull == -INFINITY ? 0.f : mfull;
-  }
+  };
+  if (n_nodes == 1)
+    passes(Flag<true>{});
+  else
+    passes(Flag<false>{});
 
   // ---- finalize: denominators of all four head blocks through LDS
   const float lt = half_sum(l_run);
