@@ -33,19 +33,28 @@ __device__ __forceinline__ unsigned ordered_key(float w) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int kCtrl, int kRowMask = 0xF>
-__device__ __forceinline__ unsigned dpp_max(unsigned v) {
-  return max(v, (unsigned)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, kRowMask, 0xF, false));
-}
-
-// Maximum of v over the 64 lanes, returned to every lane.
+// Maximum of v over the 64 lanes, returned to every lane: row shifts by 1, 2, 4, 8 leave each
+// row's maximum in its lane 15, then row broadcasts of lane 15 into rows 1, 3 and of lane 31
+// into rows 2, 3 leave the wave's maximum in lane 63.  Each step is one max with a DPP source; a
+// lane without a source (or outside the row mask) is not written and keeps its value.  A DPP
+// read of a VGPR written by the previous VALU instruction needs two wait states (s_nop 1), and
+// so does the lane read that follows.
 __device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
-  v = dpp_max<0x111>(v);  // row_shr:1
-  v = dpp_max<0x112>(v);  // row_shr:2
-  v = dpp_max<0x114>(v);  // row_shr:4
-  v = dpp_max<0x118>(v);  // row_shr:8   -> lane 15 of each row: the row's maximum
-  v = dpp_max<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
-  v = dpp_max<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3 -> lane 63: the wave's maximum
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "+v"(v));
   return __builtin_amdgcn_readlane(v, 63);
 }
 
@@ -117,9 +126,14 @@ __global__ void __launch_bounds__(64) tree_build_kernel(BuildArgs a) {
     my_anc = me ? (pa | (1ull << idx)) : my_anc;
     if (step + 1 == B) break;  // no further pops: nothing to offer
     // offer the next sibling (the pages' float32 expression, in this order), then the first child
+    // (the three reads are unconditional, with indices clamped into the table, so that they are
+    // issued together and waited for once)
     const bool has_sib = r + 1 < K, has_child = d < D;
-    const float ws = has_sib ? (w - lp_s[(d - 1) * K + r]) + lp_s[(d - 1) * K + r + 1] : 0.f;
-    const float wc = has_child ? w + lp_s[d * K] : 0.f;
+    const float lp_r = lp_s[(d - 1) * K + r];
+    const float lp_n = lp_s[(d - 1) * K + min(r + 1, K - 1)];
+    const float lp_c = lp_s[min(d, D - 1) * K];
+    const float ws = has_sib ? (w - lp_r) + lp_n : 0.f;
+    const float wc = has_child ? w + lp_c : 0.f;
     const int slot_s = n_ins, slot_c = n_ins + (has_sib ? 1 : 0);
     n_ins = slot_c + (has_child ? 1 : 0);
     // per lane: does this lane own the sibling's / the child's slot, in sub-slot 0 or 1?
