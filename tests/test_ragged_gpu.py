@@ -38,6 +38,28 @@ def test_ragged_verify(lib, q, splits):
     assert_close(out, lse, ro, rl, f"ragged q={q} splits={splits}")
 
 
+@pytest.mark.parametrize("s_count", [13, 27, 64, 65])
+def test_ragged_stream_counts(lib, s_count):
+    """Ragged launches of up to 64 streams place the streams on the XCDs by prefix length (a
+    ranking with ties, dealt in snake order with a partial last round when the count is not a
+    multiple of 8); above 64 they keep the plain order.  Every stream must be computed exactly
+    once: the outputs start as NaN and every stream is checked against the oracle."""
+    q = 9
+    rng = np.random.default_rng(300 + s_count)
+    prefixes = rng.integers(0, 260, size=s_count)
+    prefixes[::5] = 128  # ties
+    prefixes = [int(x) for x in prefixes]
+    print(f"[ragged] {s_count} streams, prefixes in [0, 260)", flush=True)
+    b = ragged_batch(400 + s_count, prefixes, q)
+    out = torch.full((s_count, q, synth.HEADS, 512), float("nan"), dtype=torch.float32, device="cuda:0")
+    lse = torch.full((s_count, q, synth.HEADS), float("nan"), dtype=torch.float32, device="cuda:0")
+    lib.verify_attn_ragged(dev_bf16(b.q_lat), dev_bf16(b.q_pe), dev_bf16(b.ckv), dev_bf16(b.kpe),
+                           dev_i32(np.array(prefixes)), max(prefixes), dev_i32(b.parents), out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.verify_attn_ragged(b.q_lat, b.q_pe, b.ckv, b.kpe, prefixes, b.parents)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, f"ragged {s_count} streams")
+
+
 def test_equal_prefixes_match_uniform_call_bitwise(lib):
     p, q = 700, 33
     b = synth.random_inputs(8, 4, p, q)

@@ -152,6 +152,42 @@ __device__ __forceinline__ void score_step(f32x16& st, const bf16x8& k, const bf
 __device__ __forceinline__ float half_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float half_sum(float x) { return x + __shfl_xor(x, 32); }
 
+// Ragged launches: the stream that logical stream ls stands for.  Each XCD runs a contiguous
+// run of logical streams; with per-stream prefixes of different lengths, runs of consecutive
+// streams carry unequal work and the busiest XCD sets the launch time.  So the streams are
+// ranked by prefix length (longest first, ties by index; an invalid entry counts as 0) and the
+// ranks are dealt to the 8 runs in snake order -- runs 0..7 take ranks 0..7, runs 7..0 ranks
+// 8..15, and so on, with a last partial round for n_streams % 8 -- which evens out the runs'
+// totals; within a run the streams come longest first.  One stream per lane: at most 64 streams.
+// Every wave of the launch computes the same mapping.
+__device__ __forceinline__ int balanced_stream(const int32_t* prefix_lens, int n_streams, int max_prefix, int ls,
+                                               int lane) {
+  const int S = n_streams;
+  int len = -1;
+  if (lane < S) {
+    const int pv = prefix_lens[lane];
+    len = (pv < 0 || pv > max_prefix) ? 0 : pv;
+  }
+  int rank = 0;
+  for (int j = 0; j < S; ++j) {
+    const int lj = __builtin_amdgcn_readlane(len, j);
+    rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+  }
+  // run b holds S / 8 streams from the full rounds, plus one from the partial round when that
+  // round (forward after an even number of full rounds, backward after an odd one) reaches it
+  const int full = S >> 3, part = S & 7;
+  int b = 0, start = 0;
+  for (; b < 7; ++b) {
+    const int extra = part == 0 ? 0 : ((full & 1) == 0 ? (b < part) : (b >= 8 - part));
+    if (ls < start + full + extra) break;
+    start += full + extra;
+  }
+  const int i = ls - start;
+  const int rk = 8 * i + ((i & 1) ? 7 - b : b);
+  const unsigned long long m = __builtin_amdgcn_ballot_w64(lane < S && rank == rk);
+  return m != 0 ? (int)__builtin_ctzll(m) : ls;
+}
+
 template <bool B>
 struct Flag {
   static constexpr bool value = B;
@@ -175,7 +211,8 @@ verify_attn_kernel(VerifyArgs a) {
   // two halves reach those bursts at different times.  Workgroup b is dispatched to XCD b % 8;
   // within a group the index is renumbered so that each XCD runs a contiguous run of (stream,
   // node pair, split) units: the workgroups of one stream then share that XCD's L2 while they
-  // stream the same key tiles, and the light workgroups of group 1 spread over all XCDs.
+  // stream the same key tiles, and the light workgroups of group 1 spread over all XCDs.  In a
+  // ragged launch the logical stream is mapped to a real one by length (balanced_stream).
   const int b_id = (int)blockIdx.x;
   const int grp = (b_id >= a.lead1 && b_id < a.lead1 + a.wg_count0) ? 0 : 1;
   const int j = grp == 0 ? b_id - a.lead1 : (b_id < a.lead1 ? b_id : b_id - a.wg_count0);
@@ -186,8 +223,11 @@ verify_attn_kernel(VerifyArgs a) {
   const int n_split = a.splits[grp];
   const int sp = logical % n_split;
   const int unit = logical / n_split;
-  const int s = grp == 0 ? unit / max(a.n_pairs, 1) : unit;
-  const int pair = grp == 0 ? unit - s * a.n_pairs : 0;
+  const int ls = grp == 0 ? unit / max(a.n_pairs, 1) : unit;  // logical stream
+  const int s = (a.prefix_lens != nullptr && a.n_streams <= 64)
+                    ? balanced_stream(a.prefix_lens, a.n_streams, a.prefix_len, ls, lane)
+                    : ls;
+  const int pair = grp == 0 ? unit - ls * a.n_pairs : 0;
   const int q0 = grp == 0 ? 2 * pair : a.q_len - 1;  // first node of the workgroup
   const int n_nodes = grp == 0 ? 2 : 1;
 
