@@ -383,8 +383,8 @@ def main() -> int:
         print(summarize_pmc(f, w, cf, cw, int(nbytes), cmds), end="")
         return 0
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
-                                   "(streams shard across GPUs with no communication; see DESIGN.md)"}))
+        print(json.dumps({"error": "the benchmark runs on exactly one GPU; --gpus must be 1 "
+                                   "(streams would shard across GPUs with no communication between them)"}))
         return 2
 
     import torch
