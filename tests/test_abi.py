@@ -275,10 +275,18 @@ def test_automatic_split_plan_on_the_five_workloads():
     """The plan the library picks for each seeded workload on a 256-CU part (the count it assumes
     when no device answers).  These are the plans measured best, or within 2% of the best, in a
     sweep of forced split counts on the GPU; the reported count is the larger group's."""
-    assert _lib.num_splits(256, 9, 1, 0) == 1        # one stream, 9 tiles: no merge pays off
+    assert _lib.num_splits(256, 9, 1, 0) == 5        # one stream, 9 tiles: 5 splits of 2, one merge
     assert _lib.num_splits(1024, 33, 8, 0) == 1      # 136 workgroups fit at once: no split
     assert _lib.num_splits(1024, 9, 64, 0) == 4      # the odd node split 4 ways, pairs whole
-    assert _lib.num_splits(4096, 33, 1, 0) == 15     # one long stream: 15 splits of 9 tiles
+    assert _lib.num_splits(4096, 33, 1, 0) == 10     # one long stream: 10 splits of 13 tiles
     assert _lib.num_splits(4096, 33, 64, 0) == 4     # 1024 pair workgroups = 4 rounds; odd node x4
     assert _lib.workspace_size(1024, 33, 8, 0) == 0  # unsplit: no workspace
-    assert _lib.workspace_size(4096, 33, 64, 0) > 0
+
+    def ws(rows0, splits0, rows1, splits1):  # partial out + lse per split group, 256-B aligned
+        al = lambda x: (x + 255) // 256 * 256
+        return (al(splits0 * rows0 * 2048) + al(splits1 * rows1 * 2048) + al(splits0 * rows0 * 4)
+                + al(splits1 * rows1 * 4))
+    # the long stream's 16 node pairs (2048 query-head rows) and its odd node, 10 splits each
+    assert _lib.workspace_size(4096, 33, 1, 0) == ws(2048, 10, 64, 10)
+    assert _lib.workspace_size(256, 9, 1, 0) == ws(512, 5, 64, 5)
+    assert _lib.workspace_size(4096, 33, 64, 0) == ws(0, 1, 64 * 64, 4)

@@ -74,8 +74,10 @@ void set_splits(Plan& p, int g, int want) {
 // decides.  Otherwise, when group 0 fills whole rounds, group 1 adds rounds of its own; else the
 // estimate is the larger of group 0's own rounds and the list-scheduling bound (total work /
 // CUs + one group-1 workgroup).  A split group pays for its partials: 2 KiB per row written and
-// read back by the merge (~0.06 tile-times per 128 rows of one split on the whole GPU's
-// bandwidth) plus about 3 tile-times for the merge launch (measured: a merge costs ~3 us).
+// read back by the merge, plus the split workgroup's own Q load (~0.09 tile-times per 128 rows
+// of one split, fitted to forced-split sweeps of a long single stream); a launch with any split
+// group pays about 3 tile-times once for the merge launch that covers both groups (measured: a
+// merge costs ~3 us).
 double plan_cost(const Plan& p, long long units0, long long units1, int cus) {
   const double c0 = p.tiles_per_split[0], c1 = p.tiles_per_split[1];
   const long long n0 = units0 * p.splits[0], n1 = units1 * p.splits[1];
@@ -89,8 +91,10 @@ double plan_cost(const Plan& p, long long units0, long long units1, int cus) {
     else
       t = fmax(end0, ((double)n0 * c0 + (double)n1 * c1) / cus + c1);
   }
-  if (n0 && p.splits[0] > 1) t += 0.06 * (double)n0 + 3.0;
-  if (n1 && p.splits[1] > 1) t += 0.03 * (double)n1 + 3.0;
+  const bool split0 = n0 && p.splits[0] > 1, split1 = n1 && p.splits[1] > 1;
+  if (split0) t += 0.09 * (double)n0;
+  if (split1) t += 0.045 * (double)n1;
+  if (split0 || split1) t += 3.0;  // one merge launch covers both groups
   return t;
 }
 
@@ -112,7 +116,13 @@ Plan make_plan(int prefix_len, int q_len, int n_streams, int num_splits) {
       if (units0 == 0 && s0 > 1) break;
       set_splits(trial, 0, s0);
       if (trial.splits[0] != s0) continue;
-      for (int s1 = 1; s1 <= kMaxSplits && s1 <= p.n_tiles; s1 *= 2) {
+      // group 1: powers of two, and group 0's own count (the odd node's workgroups then run as
+      // long as the pairs')
+      int cand[8], n_cand = 0;
+      for (int s1 = 1; s1 <= kMaxSplits && s1 <= p.n_tiles; s1 *= 2) cand[n_cand++] = s1;
+      if ((s0 & (s0 - 1)) != 0) cand[n_cand++] = s0;
+      for (int ci = 0; ci < n_cand; ++ci) {
+        const int s1 = cand[ci];
         if (units1 == 0 && s1 > 1) break;
         set_splits(trial, 1, s1);
         const double c = plan_cost(trial, units0, units1, cus);
@@ -264,16 +274,16 @@ int verify_impl(const void* q_lat, const void* q_pe, const void* ckv, const void
     }
   }
   if (ddtree::launch_verify(a, (int)blocks, stream) != hipSuccess) return DDTREE_ERR_HIP;
-  for (int g = 0; g < 2; ++g) {
-    if (!a.part_out[g]) continue;
+  if (a.part_out[0] || a.part_out[1]) {  // one merge launch for every split group
     ddtree::CombineArgs c{};
-    c.part_out = a.part_out[g];
-    c.part_lse = a.part_lse[g];
+    for (int g = 0; g < 2; ++g) {
+      c.part_out[g] = a.part_out[g];
+      c.part_lse[g] = a.part_lse[g];
+      c.rows[g] = a.part_out[g] ? plan.part_rows[g] : 0;
+      c.n_splits[g] = plan.splits[g];
+    }
     c.out = out_lat;
     c.lse = lse;
-    c.rows = (int)plan.part_rows[g];
-    c.n_splits = plan.splits[g];
-    c.group = g;
     c.n_pairs = plan.n_pairs;
     c.q_len = q_len;
     if (ddtree::launch_combine(c, stream) != hipSuccess) return DDTREE_ERR_HIP;

@@ -52,14 +52,15 @@ struct VerifyArgs {
 
 hipError_t launch_verify(const VerifyArgs& a, int wg_total, hipStream_t stream);
 
+// One merge launch covers the partial rows of both groups: group 0's rows first, then group
+// 1's (row numbering above).  A group that is not split has no rows here.
 struct CombineArgs {
-  const float* part_out;
-  const float* part_lse;
+  const float* part_out[2];
+  const float* part_lse[2];
   float* out;
   float* lse;
-  int rows;            // partial rows of the group
-  int n_splits;
-  int group;           // 0 or 1 (row numbering above)
+  long long rows[2];   // partial rows of each group, 0 when the group is not split
+  int n_splits[2];
   int n_pairs;
   int q_len;
 };

@@ -652,24 +652,33 @@ verify_attn_kernel(VerifyArgs a) {
 }
 
 // Merge of key-range splits by log-sum-exp: lse = log sum_k exp(lse_k),
-// out = sum_k exp(lse_k - lse) out_k.  One thread per (partial row, 4 dims).  The splits are
-// read in chunks of kMergeChunk with every load of a chunk in flight, and merged online: the
-// running sums are rescaled when a chunk raises the running max.  (A loop with one split per
-// iteration waits out a full memory latency per split, which dominated at tens of splits.)
+// out = sum_k exp(lse_k - lse) out_k.  One thread per (partial row, 4 dims), over the split rows
+// of both groups in one launch.  The splits are read in chunks of kMergeChunk with every load of
+// a chunk in flight, and merged online: the running sums are rescaled when a chunk raises the
+// running max.  (A loop with one split per iteration waits out a full memory latency per
+// split, which dominated at tens of splits.)
 constexpr int kMergeChunk = 8;
 
 __global__ void __launch_bounds__(256) verify_combine_kernel(CombineArgs a) {
-  const int tid = blockIdx.x * blockDim.x + threadIdx.x;
-  const int row = tid >> 7;
-  const int c4 = tid & 127;
-  if (row >= a.rows) return;
-  int orow;
-  if (a.group == 0) {
-    const int h = row & (kHeads - 1);
-    const int k = (row >> 6) & 1;
-    const int sp_pair = row >> 7;  // s * n_pairs + p
-    const int s = sp_pair / max(a.n_pairs, 1);
-    const int p = sp_pair - s * a.n_pairs;
+  const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  long long row = tid >> 7;
+  const int c4 = (int)(tid & 127);
+  const int grp = row < a.rows[0] ? 0 : 1;
+  if (grp == 1) {
+    row -= a.rows[0];
+    if (row >= a.rows[1]) return;
+  }
+  const long long rows = a.rows[grp];
+  const int n_splits = a.n_splits[grp];
+  const float* part_out = a.part_out[grp];
+  const float* part_lse = a.part_lse[grp];
+  long long orow;
+  if (grp == 0) {
+    const int h = (int)(row & (kHeads - 1));
+    const int k = (int)((row >> 6) & 1);
+    const long long sp_pair = row >> 7;  // s * n_pairs + p
+    const long long s = sp_pair / max(a.n_pairs, 1);
+    const long long p = sp_pair - s * a.n_pairs;
     orow = (s * a.q_len + 2 * p + k) * kHeads + h;
   } else {
     orow = ((row >> 6) * a.q_len + a.q_len - 1) * kHeads + (row & (kHeads - 1));
@@ -677,7 +686,7 @@ __global__ void __launch_bounds__(256) verify_combine_kernel(CombineArgs a) {
   float mx = -INFINITY, den = 0.f;
   float poison = 0.f;  // NaN once any split is NaN (a poisoned stream), whatever the others hold
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = 0; k0 < a.n_splits; k0 += kMergeChunk) {
+  for (int k0 = 0; k0 < n_splits; k0 += kMergeChunk) {
     float lk[kMergeChunk];
     float4 v[kMergeChunk];
 #pragma unroll
@@ -685,9 +694,9 @@ __global__ void __launch_bounds__(256) verify_combine_kernel(CombineArgs a) {
       const int k = k0 + j;
       lk[j] = -INFINITY;
       v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (k < a.n_splits) {
-        lk[j] = a.part_lse[(size_t)k * a.rows + row];
-        v[j] = *reinterpret_cast<const float4*>(a.part_out + ((size_t)k * a.rows + row) * kDLat + 4 * c4);
+      if (k < n_splits) {
+        lk[j] = part_lse[(size_t)k * rows + row];
+        v[j] = *reinterpret_cast<const float4*>(part_out + ((size_t)k * rows + row) * kDLat + 4 * c4);
       }
     }
     float cmx = mx;
@@ -732,7 +741,7 @@ hipError_t launch_verify(const VerifyArgs& a, int wg_total, hipStream_t stream) 
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-  const long long threads = (long long)a.rows * 128;
+  const long long threads = (a.rows[0] + a.rows[1]) * 128;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   void* args[] = {const_cast<CombineArgs*>(&a)};
   return hipLaunchKernel(reinterpret_cast<const void*>(verify_combine_kernel), dim3(blocks), dim3(256),
