@@ -538,7 +538,7 @@ verify_attn_kernel(VerifyArgs a) {
       mx_run = -INFINITY;
 
       stage_tile(t_begin, 0);
-      if (attempt == 0) {
+      if (attempt == 0 && active) {
         const size_t qrow = ((size_t)s * Q + qc) * kHeads + head;
         const uint16_t* ql = a.q_lat + qrow * kDLat + g * 8;
 #pragma unroll
@@ -552,6 +552,15 @@ verify_attn_kernel(VerifyArgs a) {
         for (int ks = 0; ks < 4; ++ks)
           *reinterpret_cast<bf16x8*>(smem + kQpeOff + wave * 4096 + ks * 1024 + lane * 16) =
               *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+      } else if (attempt == 0) {
+        // Waves 2 and 3 of a one-node workgroup only keep the workgroup's schedule: their
+        // scores are never read.  Zero queries make their score products draw far less power
+        // than a second copy of the real ones (the launch is power-bound).
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) qf[ks] = bf16x8{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          *reinterpret_cast<bf16x8*>(smem + kQpeOff + wave * 4096 + ks * 1024 + lane * 16) = bf16x8{};
       }
       int t = t_begin;
       // first tile: sets the reference max on the first pass, no value product yet
