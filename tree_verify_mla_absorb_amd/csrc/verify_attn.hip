@@ -604,12 +604,13 @@ verify_attn_kernel(VerifyArgs a) {
   else
     passes(Flag<false>{});
 
-  // ---- finalize: denominators of all four head blocks through LDS
+  // ---- finalize: reciprocal denominators of all four head blocks through LDS
   const float lt = half_sum(l_run);
-  float* l_sh = reinterpret_cast<float*>(smem + kPOff);  // the P buffers are free after the last barrier
-  if (g == 0) l_sh[wave * 32 + c32] = lt;
-  const int part_rows = grp == 0 ? a.n_streams * a.n_pairs * 2 * kHeads : a.n_streams * kHeads;
   const float poison = bad_prefix ? __builtin_nanf("") : 0.f;
+  // 1 / denominator of every row, once per row (the P buffers are free after the last barrier)
+  float* inv_sh = reinterpret_cast<float*>(smem + kPOff);
+  if (g == 0) inv_sh[wave * 32 + c32] = (lt > 0.f ? 1.0f / lt : 0.f) + poison;
+  const int part_rows = grp == 0 ? a.n_streams * a.n_pairs * 2 * kHeads : a.n_streams * kHeads;
   if (active && g == 0) {
     const float lse_v = (lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY) + poison;
     if (n_split == 1)
@@ -645,8 +646,7 @@ verify_attn_kernel(VerifyArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int r = 2 * j + (lane >> 5);
-      const float lh = l_sh[hb * 32 + r];
-      const float inv = (lh > 0.f ? 1.0f / lh : 0.f) + poison;
+      const float inv = inv_sh[hb * 32 + r];
       float4 v = *reinterpret_cast<const float4*>(tbuf + r * kTRow + (lane & 31) * 16);
       v.x *= inv;
       v.y *= inv;
