@@ -665,9 +665,9 @@ verify_attn_kernel(VerifyArgs a) {
 // of both groups in one launch.  The splits are read in chunks of kMergeChunk with every load of
 // a chunk in flight, and merged online: the running sums are rescaled when a chunk raises the
 // running max.  (A loop with one split per iteration waits out a full memory latency per
-// split, which dominated at tens of splits.)
-constexpr int kMergeChunk = 8;
-
+// split, which dominated at tens of splits.)  A launch whose groups have at most 4 splits (the
+// usual case) uses chunks of 4: half the registers, so more rows' loads are in flight per CU.
+template <int kMergeChunk>
 __global__ void __launch_bounds__(256) verify_combine_kernel(CombineArgs a) {
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   long long row = tid >> 7;
@@ -753,8 +753,10 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const long long threads = (a.rows[0] + a.rows[1]) * 128;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   void* args[] = {const_cast<CombineArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(verify_combine_kernel), dim3(blocks), dim3(256),
-                         args, 0, stream);
+  const int s0 = a.rows[0] ? a.n_splits[0] : 0, s1 = a.rows[1] ? a.n_splits[1] : 0;
+  const void* kernel = (s0 > s1 ? s0 : s1) <= 4 ? reinterpret_cast<const void*>(verify_combine_kernel<4>)
+                                                : reinterpret_cast<const void*>(verify_combine_kernel<8>);
+  return hipLaunchKernel(kernel, dim3(blocks), dim3(256), args, 0, stream);
 }
 
 }  // namespace ddtree
