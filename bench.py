@@ -459,9 +459,15 @@ def main() -> int:
     if not args.no_detail_tables:
         fused_us = time_calls(lambda: _lib.accept_compact(ckv, kpe, w.prefix, parents, draft_tok, target_tok,
                                                           keep=keep, n_keep=n_keep, next_token=next_tok))
+        compact_us = time_calls(lambda: _lib.compact_kv(ckv, kpe, w.prefix, keep, n_keep))
+        # read + write of every kept row that moves (a row kept in place, such as the root, is skipped)
+        compact_moved = 2 * (512 + 64) * 2 * sum(int((b.keep[s, :b.n_keep[s]] != np.arange(b.n_keep[s])).sum())
+                                                 for s in range(w.streams))
         tables = {
             "accept_compact_us_per_call": round(fused_us, 2),
-            "compact_kv_us_per_call": round(time_calls(lambda: _lib.compact_kv(ckv, kpe, w.prefix, keep, n_keep)), 2),
+            "compact_kv_us_per_call": round(compact_us, 2),
+            "compact_kv_moved_bytes": compact_moved,
+            "compact_kv_gbs": round(compact_moved / (compact_us * 1e-6) / 1e9, 1),
             "tree_accept_us_per_call": accept_table(_lib, dev),
             "tree_build_us_per_call": build_table(_lib, dev),
             "accept_compact_layers": layers_table(_lib, dev, w, parents, draft_tok, target_tok, b.keep, b.n_keep),
