@@ -58,6 +58,9 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+// kOneSlot: budget <= 32, so at most 1 + 2 (budget - 1) <= 63 candidates ever exist and every
+// one fits in sub-slot 0; the second sub-slot's keys, ballot and inserts are compiled out.
+template <bool kOneSlot>
 __global__ void __launch_bounds__(64) tree_build_kernel(BuildArgs a) {
   __shared__ float lp_s[kBuildMaxD * kBuildMaxK];
   __shared__ int tok_s[kBuildMaxD * kBuildMaxK];
@@ -88,14 +91,14 @@ __global__ void __launch_bounds__(64) tree_build_kernel(BuildArgs a) {
   int n = 1, n_ins = 1;
   for (int step = 0; step < B; ++step) {
     const unsigned k0 = l0 ? ordered_key(w0) : 0u;
-    const unsigned k1 = l1 ? ordered_key(w1) : 0u;
+    const unsigned k1 = (!kOneSlot && l1) ? ordered_key(w1) : 0u;
     const unsigned m = wave_max_u32(max(k0, k1));
     if (m == 0) break;  // no candidate left (top-1 chain shorter than the budget)
     const unsigned long long b0 = __builtin_amdgcn_ballot_w64(k0 == m);
-    const unsigned long long b1 = __builtin_amdgcn_ballot_w64(k1 == m);
+    const unsigned long long b1 = kOneSlot ? 0ull : __builtin_amdgcn_ballot_w64(k1 == m);
     int d, r, p;
     float w;
-    if (b0 != 0) {  // uniform: the earliest-inserted maximum sits in sub-slot 0 of lane `owner`
+    if (kOneSlot || b0 != 0) {  // uniform: the earliest-inserted maximum sits in sub-slot 0 of lane `owner`
       const int owner = (int)__builtin_ctzll(b0);
       w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(w0), owner));
       d = __builtin_amdgcn_readlane(d0, owner);
@@ -138,8 +141,8 @@ __global__ void __launch_bounds__(64) tree_build_kernel(BuildArgs a) {
     n_ins = slot_c + (has_child ? 1 : 0);
     // per lane: does this lane own the sibling's / the child's slot, in sub-slot 0 or 1?
     const bool own_s = has_sib && lane == (slot_s & 63), own_c = has_child && lane == (slot_c & 63);
-    const bool s_in0 = own_s && slot_s < 64, s_in1 = own_s && slot_s >= 64;
-    const bool c_in0 = own_c && slot_c < 64, c_in1 = own_c && slot_c >= 64;
+    const bool s_in0 = own_s && (kOneSlot || slot_s < 64), s_in1 = !kOneSlot && own_s && slot_s >= 64;
+    const bool c_in0 = own_c && (kOneSlot || slot_c < 64), c_in1 = !kOneSlot && own_c && slot_c >= 64;
     w0 = s_in0 ? ws : (c_in0 ? wc : w0);
     d0 = s_in0 ? d : (c_in0 ? d + 1 : d0);
     r0 = s_in0 ? r + 1 : (c_in0 ? 0 : r0);
@@ -178,8 +181,9 @@ __global__ void __launch_bounds__(64) tree_build_kernel(BuildArgs a) {
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<BuildArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(tree_build_kernel), dim3((unsigned)a.n_streams), dim3(64),
-                         args, 0, stream);
+  const void* kernel = a.budget <= 32 ? reinterpret_cast<const void*>(tree_build_kernel<true>)
+                                      : reinterpret_cast<const void*>(tree_build_kernel<false>);
+  return hipLaunchKernel(kernel, dim3((unsigned)a.n_streams), dim3(64), args, 0, stream);
 }
 
 }  // namespace ddtree
