@@ -119,7 +119,12 @@ __global__ void __launch_bounds__(64) tree_build_kernel(BuildArgs a) {
     const unsigned long long pa =
         (unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(unsigned)(my_anc & 0xffffffffu), p) |
         ((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(unsigned)(my_anc >> 32), p) << 32);
+    // the node's token and the three log-probabilities its offers need, read together (indices
+    // clamped into the table) so that one LDS wait covers them all
     const int t = tok_s[(d - 1) * K + r];
+    const float lp_r = lp_s[(d - 1) * K + r];
+    const float lp_n = lp_s[(d - 1) * K + min(r + 1, K - 1)];
+    const float lp_c = lp_s[min(d, D - 1) * K];
     const bool me = lane == idx;
     my_parent = me ? p : my_parent;
     my_depth = me ? d : my_depth;
@@ -127,14 +132,11 @@ __global__ void __launch_bounds__(64) tree_build_kernel(BuildArgs a) {
     my_tok = me ? t : my_tok;
     my_w = me ? w : my_w;
     my_anc = me ? (pa | (1ull << idx)) : my_anc;
-    if (step + 1 == B) break;  // no further pops: nothing to offer
-    // offer the next sibling (the pages' float32 expression, in this order), then the first child
-    // (the three reads are unconditional, with indices clamped into the table, so that they are
-    // issued together and waited for once)
+    // offer the next sibling (the pages' float32 expression, in this order), then the first child.
+    // The last pop's offers are made too (nothing reads the pool after the loop; in the one-slot
+    // form the last child may take slot 64, which lands on slot 0 and is never read): without a
+    // branch here the reads above are not sunk below it.
     const bool has_sib = r + 1 < K, has_child = d < D;
-    const float lp_r = lp_s[(d - 1) * K + r];
-    const float lp_n = lp_s[(d - 1) * K + min(r + 1, K - 1)];
-    const float lp_c = lp_s[min(d, D - 1) * K];
     const float ws = has_sib ? (w - lp_r) + lp_n : 0.f;
     const float wc = has_child ? w + lp_c : 0.f;
     const int slot_s = n_ins, slot_c = n_ins + (has_sib ? 1 : 0);
