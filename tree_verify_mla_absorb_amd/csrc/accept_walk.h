@@ -36,9 +36,11 @@ __device__ __forceinline__ Walk accept_walk(const int32_t* parents, const int32_
   const bool ok = !in || (lane == 0 ? p == -1 : (p >= 0 && p < lane));
   Walk w{0, -1, 0};
   if (__builtin_amdgcn_ballot_w64(!ok) != 0) return w;  // uniform
+  // cur is wave-uniform (the lowest bit of a ballot), so the target token at cur is a lane read,
+  // not an LDS permute round trip per level
   int cur = 0, n = 1;
   for (int level = 1; level < q_len; ++level) {
-    const int tc = __shfl(tg, cur);
+    const int tc = __builtin_amdgcn_readlane(tg, cur);
     const unsigned long long m = __builtin_amdgcn_ballot_w64(in && p == cur && d == tc);
     if (m == 0) break;
     cur = (int)__builtin_ctzll(m);
@@ -46,7 +48,7 @@ __device__ __forceinline__ Walk accept_walk(const int32_t* parents, const int32_
     ++n;
   }
   w.n = n;
-  w.next = __shfl(tg, cur);
+  w.next = __builtin_amdgcn_readlane(tg, cur);
   return w;
 }
 
