@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(64 * kAppendWaves) append_tree_kv_kernel(Appen
     if (i == 0 && lane == 0 && a.status != nullptr) atomicOr(a.status, why);
     return;
   }
-  const int pos = P + __shfl(depth, i);
+  const int pos = P + __builtin_amdgcn_readlane(depth, i);  // i is the wave's node: a lane read
 
   const float* x = a.kv + ((size_t)s * Q + i) * (kDLat + kDRope);
   const F32x4 x0 = *reinterpret_cast<const F32x4*>(x + 8 * lane);
