@@ -156,16 +156,17 @@ __global__ void __launch_bounds__(64) tree_build_kernel(BuildArgs a) {
     p1 = s_in1 ? p : (c_in1 ? idx : p1);
     l1 = l1 || s_in1 || c_in1;
   }
-  // Retrieve links, from the parents: children of a node were appended in rank order, so the
-  // first child is the lowest index with that parent and the next sibling the next such index.
-  int my_fc = -1, my_ns = -1;
-  for (int j = 0; j < n; ++j) {
-    const int pj = __builtin_amdgcn_readlane(my_parent, j);
-    const unsigned long long kids = __builtin_amdgcn_ballot_w64(lane < n && my_parent == j);
-    if (lane == j) my_fc = kids != 0 ? (int)__builtin_ctzll(kids) : -1;
-    const unsigned long long sibs = __builtin_amdgcn_ballot_w64(lane < n && lane > j && my_parent == pj);
-    if (lane == j && j > 0) my_ns = sibs != 0 ? (int)__builtin_ctzll(sibs) : -1;
-  }
+  // Retrieve links from a (parent, rank) table: the children of a node are appended in rank
+  // order 0, 1, 2, ... (rank r + 1 is offered only once rank r is popped), so its first child is
+  // entry (node, 0) and a node's next sibling is entry (parent, rank + 1); -1 where none.
+  __shared__ __attribute__((aligned(16))) int link_s[kBuildMaxD * kBuildMaxK];  // [parent < 64][rank < 64]
+  typedef int I32x4 __attribute__((ext_vector_type(4)));
+  for (int e = 4 * lane; e < n * 64; e += 4 * 64) *reinterpret_cast<I32x4*>(link_s + e) = I32x4{-1, -1, -1, -1};
+  __syncthreads();
+  if (lane > 0 && lane < n) link_s[my_parent * 64 + my_rank] = lane;
+  __syncthreads();
+  const int my_fc = lane < n ? link_s[lane * 64] : -1;
+  const int my_ns = (lane > 0 && lane < n && my_rank + 1 < K) ? link_s[my_parent * 64 + my_rank + 1] : -1;
   const size_t row = (size_t)s * (B + 1) + lane;
   if (lane < n) {
     a.parents[row] = my_parent;
