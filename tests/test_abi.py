@@ -110,6 +110,9 @@ def test_split_queries():
     assert _lib.num_splits(100, 9, 1, 32) == 4        # 109 keys: four tiles
     assert _lib.num_splits(4096, 33, 1, 13) == 13     # 130 tiles: 10 per split
     assert _lib.num_splits(4096, 33, 1, 40) == 33     # 130 tiles: 4 per split -> 33 splits
+    assert _lib.num_splits(8192, 17, 1, 64) == 52     # 257 tiles: 5 per split -> 52 splits
+    assert _lib.num_splits(8192, 17, 1, 1000) == 52   # requests above 64 are taken as 64
+    assert _lib.num_splits(100, 9, 2, 64) == 4        # never more splits than tiles
 
 
 def compact(ckv=A, kpe=C, rows=300, s=2, prefix=100, keep=E, n_keep=F, stride=33, status=None, cache=True):

@@ -59,7 +59,11 @@ def test_small_shapes_no_split(lib, s, p, q):
                                           # odd-node workgroups dispatched partly ahead of the
                                           # pairs: 25 of them (5 splits of 2 tiles; 8 first),
                                           # and 24 (8 first)
-                                          (5, 300, 9, 7), (24, 40, 3, 1)])
+                                          (5, 300, 9, 7), (24, 40, 3, 1),
+                                          # the 64-split maximum (257 tiles: 52 splits of 5
+                                          # tiles, seven merge chunks), a request above it, and
+                                          # a request above the tile count (4 splits of 1 tile)
+                                          (1, 8192, 17, 64), (1, 8192, 17, 1000), (2, 100, 9, 64)])
 def test_forced_and_auto_splits(lib, s, p, q, splits):
     b = synth.random_inputs(2000 + p + q, s, p, q)
     check(lib, b, p, splits=splits, what=f"split {s},{p},{q}/{splits}")
