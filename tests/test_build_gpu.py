@@ -47,7 +47,10 @@ def check_build(lib, lp, tok, budget, roots=None, what=""):
 
 
 @pytest.mark.parametrize("d,k,budget", [(8, 4, 32), (15, 8, 63), (4, 3, 20), (1, 5, 5), (64, 64, 63),
-                                        (2, 64, 63), (63, 2, 63)])
+                                        (2, 64, 63), (63, 2, 63),
+                                        # budget 33: the smallest on the two-slot pool (32 and
+                                        # below take the one-slot kernel); budget 1: one pop
+                                        (6, 16, 33), (3, 2, 1)])
 def test_build_matches_oracle(lib, d, k, budget):
     lp, tok = drafter(20 + d, 64, d, k)
     roots = np.arange(64, dtype=np.int32) + 1000
