@@ -97,6 +97,53 @@ def test_ties_go_in_insertion_order():
     assert t["parents"].tolist() == [-1, 0, 0, 1]
 
 
+def _rne_f32(x):
+    """Round an exact rational to the nearest float32, ties to even (normal range only), from
+    the definition: the float32 grid near |x| has spacing 2^(e - 23) with 2^e <= |x| < 2^(e+1)."""
+    from fractions import Fraction
+    if x == 0:
+        return Fraction(0)
+    e = abs(x.numerator).bit_length() - abs(x.denominator).bit_length()
+    while Fraction(2) ** e > abs(x):
+        e -= 1
+    while Fraction(2) ** (e + 1) <= abs(x):
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    q = x / ulp
+    n = q.numerator // q.denominator
+    rest = q - n
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n * ulp
+
+
+def test_sibling_weight_evaluated_in_the_pages_order():
+    """The pages fix one expression for bit parity: a sibling's weight is
+    ``logw - lp[d-1, r] + lp[d-1, r+1]`` in float32, left to right ("Building the Foundation",
+    sections "Tie-Breaking and Numerical Precision" and "Assumptions Underlying the Design",
+    Assumption 4).  With lp = [[-0.61, -1.61], [-0.13, -2.38]] the depth-2, rank-1 sibling of
+    node 1 has, by exact arithmetic with one float32 rounding per operation:
+      w = rn(-0.61 + -0.13) = -0.74 (0xbf3d70a4)
+      rn(rn(w - -0.13) + -2.38) = 0xc03f5c2a   (the pages' order)
+      rn(w + rn(-2.38 - -0.13)) = 0xc03f5c29   (reassociated: one ulp apart)
+    The oracle must produce the first."""
+    from fractions import Fraction
+
+    lp = np.array([[-0.61, -1.61], [-0.13, -2.38]], np.float32)
+    tok = np.array([[10, 11], [20, 21]], np.int32)
+    x = {name: Fraction(float(v)) for name, v in (("a0", lp[0, 0]), ("b0", lp[1, 0]), ("b1", lp[1, 1]))}
+    w = _rne_f32(x["a0"] + x["b0"])
+    pages = _rne_f32(_rne_f32(w - x["b0"]) + x["b1"])
+    reassoc = _rne_f32(w + _rne_f32(x["b1"] - x["b0"]))
+    bits = lambda v: int(np.array([float(v)], np.float32).view(np.uint32)[0])  # exact: v is on the grid
+    assert bits(w) == 0xBF3D70A4
+    assert bits(pages) == 0xC03F5C2A and bits(reassoc) == 0xC03F5C29
+    t = ob.tree_build(lp, tok, 6)  # the whole 2 + 4 node product tree
+    idx = [i for i in range(t["n_nodes"]) if t["depths"][i] == 2 and t["ranks"][i] == 1 and t["parents"][i] == 1]
+    assert len(idx) == 1
+    assert int(t["logw"][idx[0]:idx[0] + 1].view(np.uint32)[0]) == 0xC03F5C2A
+
+
 def test_rejects_budget_out_of_range():
     lp, tok = synth.drafter_topk(1, 0, 3, 2)
     for b in (0, 64):
@@ -109,7 +156,7 @@ def test_pins_catch_planted_mistakes(monkeypatch):
 
     ORIG = ob.tree_build
 
-    def variant(wrong_row=False, child_first=False):
+    def variant(wrong_row=False, child_first=False, reassoc=False):
         def build(lp, tok, budget, root_token=-1):
             lp = np.asarray(lp, np.float32)
             d_max, k = lp.shape
@@ -122,7 +169,10 @@ def test_pins_catch_planted_mistakes(monkeypatch):
                 pushes = []
                 if r + 1 < k:
                     row = d if (wrong_row and d < d_max) else d - 1
-                    ws = np.float32(np.float32(w - lp[d - 1, r]) + lp[row, r + 1])
+                    if reassoc:  # w + (lp[r+1] - lp[r]): the same real number, another rounding
+                        ws = np.float32(w + np.float32(lp[row, r + 1] - lp[d - 1, r]))
+                    else:
+                        ws = np.float32(np.float32(w - lp[d - 1, r]) + lp[row, r + 1])
                     pushes.append((-ws, d, r + 1, p, ws))
                 if d < d_max:
                     wc = np.float32(w + lp[d, 0])
@@ -139,7 +189,8 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         return build
 
     for mutant, pin in ((variant(wrong_row=True), test_weights_order_structure_and_links),
-                        (variant(child_first=True), test_ties_go_in_insertion_order)):
+                        (variant(child_first=True), test_ties_go_in_insertion_order),
+                        (variant(reassoc=True), test_sibling_weight_evaluated_in_the_pages_order)):
         monkeypatch.setattr(ob, "tree_build", mutant)
         with pytest.raises(AssertionError):
             pin()
