@@ -75,11 +75,7 @@ def cpu_baseline(w, b, budget_s: float = 12.0):
     of CPU work; scaled to TFLOP/s of algorithmic work."""
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cores = oracle_threads()
     t_total, done, flops = 0.0, 0, 0.0
     while t_total < budget_s:
         s = done % w.streams
@@ -91,6 +87,68 @@ def cpu_baseline(w, b, budget_s: float = 12.0):
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"fp64 oracle, {done} stream evaluations over streams 0..{min(done, w.streams) - 1} "
                       f"of {w.streams} of workload {w.name} ({t_total:.1f} s)"}
+
+
+def oracle_threads() -> int:
+    """Threads the oracle's BLAS runs on (the host cores it uses)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def oracle_seconds_per_call(w, b, min_s: float = 1.0) -> dict:
+    """The fp64 oracle, as it stands, on every stream of workload ``w`` (batch ``b``) in order,
+    repeated until at least ``min_s`` seconds: seconds for one whole call (all streams)."""
+    import oracle
+    t_total, done = 0.0, 0
+    while t_total < min_s or done < w.streams:
+        s = done % w.streams
+        t0 = time.perf_counter()
+        oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, w.prefix, b.parents, streams=[s])
+        t_total += time.perf_counter() - t0
+        done += 1
+    return {"oracle_s_per_call": round(t_total / done * w.streams, 5), "oracle_cores": oracle_threads(),
+            "oracle_stream_evaluations": done}
+
+
+def host_info() -> dict:
+    """Versions and machine identity for the line: git HEAD (when the tree is a checkout), a hash
+    of the library sources, the ROCm and HIP versions, the GPU and the host CPU."""
+    import subprocess
+    info = {}
+    try:
+        info["git_head"] = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], stdout=subprocess.PIPE,
+                                          stderr=subprocess.DEVNULL, text=True, timeout=10).stdout.strip() or None
+    except Exception:
+        info["git_head"] = None
+    h = hashlib.sha256()
+    for sub in ("include", os.path.join("tree_verify_mla_absorb_amd", "csrc")):
+        d = os.path.join(ROOT, sub)
+        for f in sorted(os.listdir(d)):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    info["library_source_sha256"] = h.hexdigest()[:16]
+    try:
+        info["rocm_version"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        info["rocm_version"] = None
+    try:
+        import torch
+        info["torch_hip_version"] = torch.version.hip
+        info["gpu"] = torch.cuda.get_device_name(0)
+    except Exception:
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["host_cpu"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    info["host_cpus_visible"] = os.cpu_count()
+    return info
 
 
 def time_calls(fn, n: int = 100, replays: int = 5) -> float:
@@ -198,12 +256,13 @@ def layers_table(lib, dev, w, parents, draft_tok, target_tok, keep_bits, n_keep_
 MALL_BYTES = 256 << 20  # the part's last-level cache (Infinity Cache)
 
 
-def workloads_table(lib, dev, skip: str):
+def workloads_table(lib, dev, skip: str, with_oracle: bool = True):
     """``ddtree_verify_attn_ex`` (automatic split plan) us/call, TFLOP/s and % of the bf16 peak on
     every named workload but ``skip``: 100 calls in one HIP graph, best of 5 replays.  These
     workloads fit in the last-level cache, so that figure is warm; ``cold_us_per_call`` rotates
     through copies of the inputs and outputs totalling at least twice that cache, one copy per
-    call, so that every call finds its data evicted."""
+    call, so that every call finds its data evicted.  With ``with_oracle``, each entry also gives
+    the fp64 oracle's seconds for the same whole call on the host's cores."""
     import torch
     import synth
     table = {}
@@ -241,6 +300,10 @@ def workloads_table(lib, dev, skip: str):
                        "splits": lib.num_splits(w.prefix, w.q_len, w.streams, 0),
                        "cold_us_per_call": round(cold_us, 2), "cold_copies": n_copies}
         del ql, qp, ckv, kpe, out, lse, ws, copies
+        if with_oracle:
+            o = oracle_seconds_per_call(w, b)
+            table[name].update(o)
+            table[name]["oracle_over_gpu"] = round(o["oracle_s_per_call"] / (us * 1e-6), 1)
     torch.cuda.empty_cache()
     return table
 
@@ -292,9 +355,12 @@ def _db_rows(path: str, sql: str):
         con.close()
 
 
-def summarize_trace(db: str, command: str, skip: int = 0) -> str:
+def summarize_trace(db: str, command: str, skip: int = 0, bench_log: str = None) -> str:
     """Per-kernel dispatch statistics of a ``rocprofv3 --kernel-trace`` database, as text.
-    ``avg_timed_us`` leaves out each kernel's first ``skip`` dispatches (the warm-up steps)."""
+    ``avg_timed_us`` leaves out each kernel's first ``skip`` dispatches (the warm-up steps).
+    With ``bench_log`` (the profiled command's stdout), the JSON line that command printed is
+    kept beside the trace, with the verify kernel's roofline fraction recomputed from the
+    trace's own average next to the line's (which comes from HIP events in the same run)."""
     rows = _db_rows(db, "select name, start, duration from kernels order by start")
     per = {}
     for name, _, dur in rows:
@@ -307,6 +373,23 @@ def summarize_trace(db: str, command: str, skip: int = 0) -> str:
         timed = d[skip:] if len(d) > skip else d
         lines.append(f"{short:66s} {len(d):5d} {sum(d) / len(d):9.2f} {sum(timed) / len(timed):12.2f} "
                      f"{min(d):9.2f} {max(d):9.2f}")
+    if bench_log:
+        line = None
+        for text in open(bench_log):
+            if text.startswith("{") and '"metric"' in text:
+                line = json.loads(text)
+        if line is not None:
+            verify = [d for name, d in per.items() if "verify_attn_kernel" in name]
+            lines += ["", f"bench line printed by the profiled command: {json.dumps(line)}"]
+            if verify and "detail" in line and "flop_visible_pairs" in line["detail"]:
+                d = verify[0]
+                timed = d[skip:] if len(d) > skip else d
+                avg = sum(timed) / len(timed)
+                frac = line["detail"]["flop_visible_pairs"] / (avg * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
+                lines += [f"verify_attn_kernel avg_timed_us (trace): {avg:.2f}",
+                          f"verify_us_per_call (line, HIP events): {line['detail'].get('verify_us_per_call')}",
+                          f"roofline frac from the trace average: {frac:.4f}; from the line: "
+                          f"{line.get('roofline', {}).get('frac')}"]
     return "\n".join(lines) + "\n"
 
 
@@ -384,6 +467,9 @@ def main() -> int:
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DB", "COMMAND", "SKIP"),
                     help="print a per-kernel summary of a rocprofv3 kernel-trace database and exit")
+    ap.add_argument("--bench-log", default=None,
+                    help="with --summarize-trace: the profiled command's stdout, whose JSON line is kept "
+                         "beside the trace")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("DB", "COMMAND"),
                     help="print the verify launch's mean counters (MFMA utilisation, LDS) and exit")
     ap.add_argument("--summarize-pmc", nargs=6,
@@ -392,7 +478,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.summarize_trace:
         db, cmd, skip = args.summarize_trace
-        print(summarize_trace(db, cmd, int(skip)), end="")
+        print(summarize_trace(db, cmd, int(skip), args.bench_log), end="")
         return 0
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters), end="")
@@ -491,7 +577,7 @@ def main() -> int:
             "tree_build_us_per_call": build_table(_lib, dev),
             "accept_compact_layers": layers_table(_lib, dev, w, parents, draft_tok, target_tok, b.keep, b.n_keep),
             "append_tree_kv": append_table(_lib, dev, w, parents),
-            "verify_other_workloads": workloads_table(_lib, dev, w.name),
+            "verify_other_workloads": workloads_table(_lib, dev, w.name, with_oracle=not args.no_cpu_baseline),
             "verify_ragged": ragged_table(_lib, dev, w, q_lat, q_pe, ckv, kpe, b.parents),
         }
 
@@ -527,8 +613,13 @@ def main() -> int:
                    "flop_visible_pairs": flops, "wall_s_timed": round(wall, 3),
                    "kernel_source_sha256": kernel_sha()},
     }
+    res["detail"]["host"] = host_info()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, b)
+        # the same oracle timing, as seconds for the whole call (all streams)
+        rate = res["cpu_baseline"]["value"] * 1e12  # FLOP/s
+        res["detail"]["oracle_s_per_call"] = round(flops / rate, 3)
+        res["detail"]["oracle_over_gpu"] = round(flops / rate / (verify_ms * 1e-3), 1)
     print(json.dumps(res), flush=True)
     return 0
 

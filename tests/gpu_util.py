@@ -35,3 +35,38 @@ def assert_close(out, lse, ref_out, ref_lse, what=""):
     assert mo <= MAX_ABS and ao <= MEAN_ABS, f"{what}: out max {mo:.3e} mean {ao:.3e}"
     assert ml <= MAX_ABS and al <= MEAN_ABS, f"{what}: lse max {ml:.3e} mean {al:.3e}"
     return mo, ao, ml, al
+
+
+# Guard bands: a device tensor placed between two bands of canary bytes, so that a test can
+# check that a call wrote nothing outside the tensor it was given.
+GUARD_BYTES = 4096
+CANARY = 0xA5
+
+
+class Guarded:
+    """``t``: a contiguous device tensor of ``shape`` / ``dtype`` with GUARD_BYTES of CANARY bytes
+    right before and right after it in one allocation (``t`` stays 256-byte aligned)."""
+
+    def __init__(self, shape, dtype, fill=None):
+        itemsize = torch.empty((), dtype=dtype).element_size()
+        self.nbytes = int(np.prod(shape)) * itemsize
+        self.buf = torch.full((2 * GUARD_BYTES + self.nbytes,), CANARY, dtype=torch.uint8, device="cuda:0")
+        self.t = self.buf[GUARD_BYTES:GUARD_BYTES + self.nbytes].view(dtype).view(shape)
+        if fill is not None:
+            self.t.copy_(fill if isinstance(fill, torch.Tensor) else torch.as_tensor(fill))
+
+    def intact(self) -> bool:
+        b = self.buf.cpu().numpy()
+        return bool((b[:GUARD_BYTES] == CANARY).all() and (b[GUARD_BYTES + self.nbytes:] == CANARY).all())
+
+
+def guarded_bf16(bits: np.ndarray) -> Guarded:
+    """uint16 bf16 bit patterns -> a guarded torch.bfloat16 device tensor (bitwise)."""
+    g = Guarded(bits.shape, torch.bfloat16)
+    g.t.view(torch.int16).copy_(torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)))
+    return g
+
+
+def guarded_i32(a: np.ndarray) -> Guarded:
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return Guarded(a.shape, torch.int32, fill=torch.from_numpy(a))

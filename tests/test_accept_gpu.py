@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import dev_bf16, dev_i32, host_bits
+from gpu_util import Guarded, dev_bf16, dev_i32, guarded_bf16, guarded_i32, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +68,8 @@ def test_degenerate_cases(lib):
 
 
 def test_malformed_trees_flagged(lib):
+    """Malformed trees are flagged with n_keep = 0 and next_token = -1; nothing is written outside
+    keep, n_keep, next_token and the status word (guard bands of canary bytes around each)."""
     parents, draft, target, _ = synth.accept_case(5, 0, 17)
     bad = np.stack([parents] * 4).astype(np.int32)
     d = np.stack([draft] * 4)
@@ -75,12 +77,21 @@ def test_malformed_trees_flagged(lib):
     bad[1, 5] = 5      # self loop
     bad[2, 0] = 0      # root with a parent
     bad[3, 9] = 12     # forward link (would allow a cycle)
-    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    keep, n_keep, nxt = run_accept(lib, bad, d, t, status=status)
-    assert status.item() & 1
-    assert n_keep.tolist()[1:] == [0, 0, 0] and nxt.tolist()[1:] == [-1, -1, -1]
-    path, x = oracle.tree_accept(parents, draft, target)
-    assert n_keep[0] == len(path) and nxt[0] == x and np.array_equal(keep[0, : len(path)], path)
+    keep = Guarded((4, 17), torch.int32, fill=-7)
+    n_keep = Guarded((4,), torch.int32, fill=-7)
+    nxt = Guarded((4,), torch.int32, fill=-7)
+    status = Guarded((1,), torch.int32, fill=0)
+    lib.tree_accept(dev_i32(bad), dev_i32(d), dev_i32(t), keep=keep.t, n_keep=n_keep.t, next_token=nxt.t,
+                    status=status.t)
+    torch.cuda.synchronize()
+    assert status.t.item() & 1
+    k, n, x = keep.t.cpu().numpy(), n_keep.t.cpu().numpy(), nxt.t.cpu().numpy()
+    assert n.tolist()[1:] == [0, 0, 0] and x.tolist()[1:] == [-1, -1, -1]
+    path, xr = oracle.tree_accept(parents, draft, target)
+    assert n[0] == len(path) and x[0] == xr and np.array_equal(k[0, : len(path)], path)
+    assert (k[0, len(path):] == -7).all() and (k[1:] == -7).all()
+    for g in (keep, n_keep, nxt, status):
+        assert g.intact(), "write outside a buffer"
 
 
 def fused(lib, b, prefix):
@@ -105,6 +116,9 @@ def test_accept_compact_fused(lib, name):
 
 
 def test_accept_compact_planted_and_malformed(lib):
+    """The fused call on planted trees with one malformed stream, which stays untouched; nothing
+    is written outside the cache buffers, keep, n_keep, next_token and the status word (guard
+    bands of canary bytes around each)."""
     q, prefix = 33, 50
     cases = [synth.accept_case(41, s, q) for s in range(12)]
     parents = np.stack([c[0] for c in cases]).astype(np.int32)
@@ -114,8 +128,17 @@ def test_accept_compact_planted_and_malformed(lib):
     b.draft_tok = np.stack([c[1] for c in cases])
     b.target_tok = np.stack([c[2] for c in cases])
     print("[accept_compact] planted + malformed", flush=True)
-    gc, gk, keep, n_keep, nxt = fused(lib, b, prefix)
-    assert n_keep[4] == 0
+    c, k = guarded_bf16(b.ckv), guarded_bf16(b.kpe)
+    keep = Guarded((12, q), torch.int32, fill=-7)
+    n_keep = Guarded((12,), torch.int32, fill=-7)
+    nxt = Guarded((12,), torch.int32, fill=-7)
+    status = Guarded((1,), torch.int32, fill=0)
+    lib.accept_compact(c.t, k.t, prefix, dev_i32(b.parents), dev_i32(b.draft_tok), dev_i32(b.target_tok),
+                       keep=keep.t, n_keep=n_keep.t, next_token=nxt.t, status=status.t)
+    torch.cuda.synchronize()
+    gc, gk = host_bits(c.t), host_bits(k.t)
+    n_k, nx = n_keep.t.cpu().numpy(), nxt.t.cpu().numpy()
+    assert n_k[4] == 0 and nx[4] == -1 and status.t.item() & 1
     good = [s for s in range(12) if s != 4]
     rk = np.full((12, q), -1, np.int32)
     rn = np.zeros(12, np.int32)
@@ -123,7 +146,9 @@ def test_accept_compact_planted_and_malformed(lib):
         path, x = oracle.tree_accept(parents[s], b.draft_tok[s], b.target_tok[s])
         rk[s, : len(path)] = path
         rn[s] = len(path)
-        assert nxt[s] == x and n_keep[s] == len(path)
+        assert nx[s] == x and n_k[s] == len(path)
     rc, rkp = oracle.compact_kv(b.ckv, b.kpe, prefix, rk, rn)
     assert np.array_equal(gc, rc)
     assert np.array_equal(gk, rkp)
+    for g in (c, k, keep, n_keep, nxt, status):
+        assert g.intact(), "write outside a buffer"

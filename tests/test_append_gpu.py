@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import dev_bf16, dev_i32, host_bits
+from gpu_util import Guarded, dev_bf16, dev_i32, guarded_bf16, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -51,13 +51,17 @@ def run(lib, s_count, q, prefixes, rows, seed, tree="uniform", rope_rows=None, r
     rope_rows = rope_rows or (max(prefixes) + q)
     cos, sin = synth.rope_tables(rope_rows)
     cache = synth.layer_caches(seed, 1, s_count, rows)[0]
-    c, k = dev_bf16(cache[0]), dev_bf16(cache[1])
-    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    # guard bands of canary bytes around the cache and the status word: nothing may be written
+    # outside them, whatever the streams' prefixes or trees
+    gc_, gk_ = guarded_bf16(cache[0]), guarded_bf16(cache[1])
+    status = Guarded((1,), torch.int32, fill=0)
     prefix_arg = dev_i32(np.array(prefixes)) if ragged else int(prefixes[0])
-    lib.append_tree_kv(c, k, prefix_arg, dev_i32(parents), torch.from_numpy(kv).cuda(), torch.from_numpy(w).cuda(),
-                       1e-6, torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda(), status=status)
+    lib.append_tree_kv(gc_.t, gk_.t, prefix_arg, dev_i32(parents), torch.from_numpy(kv).cuda(),
+                       torch.from_numpy(w).cuda(), 1e-6, torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda(),
+                       status=status.t)
     torch.cuda.synchronize()
-    return host_bits(c), host_bits(k), cache, kv, w, cos, sin, parents, status.item()
+    assert gc_.intact() and gk_.intact() and status.intact(), "write outside a buffer"
+    return host_bits(gc_.t), host_bits(gk_.t), cache, kv, w, cos, sin, parents, status.t.item()
 
 
 @pytest.mark.parametrize("q", [1, 9, 33, 64])

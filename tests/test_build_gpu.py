@@ -75,6 +75,18 @@ def test_ties_follow_insertion_order(lib):
     check_build(lib, lp, tok, 40, what="all-equal log-probs")
 
 
+def test_signed_zero_log_probs_tie(lib):
+    """Log-probabilities of exactly 0 with either sign (a saturated drafter): -0.0 and +0.0
+    compare equal, so candidates weighing either are taken in insertion order, and the float32
+    weights keep the signs that IEEE sums give them."""
+    rng = np.random.default_rng(77)
+    lp = np.where(rng.random((16, 6, 5)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    lp[:, :, 3:] = np.float32(-1.0)
+    tok = np.arange(16 * 6 * 5, dtype=np.int32).reshape(16, 6, 5)
+    assert (np.signbit(lp[:, :, :3]).any() and (~np.signbit(lp[:, :, :3])).any())
+    check_build(lib, lp, tok, 40, what="signed zeros")
+
+
 def test_build_verify_accept_compact_chain(lib):
     """The step on the device: build the trees, verify them, accept against planted target
     tokens and compact, each stage fed by the previous stage's device outputs."""

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import dev_bf16, dev_i32, host_bits
+from gpu_util import Guarded, dev_bf16, dev_i32, guarded_bf16, guarded_i32, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +83,9 @@ def test_random_increasing_subsets(lib):
 
 
 def test_invalid_keep_is_flagged_and_stream_untouched(lib):
+    """Invalid keep rows are flagged and their streams left untouched; nothing is written outside
+    the cache buffers or the status word, and keep / n_keep are only read (guard bands of canary
+    bytes on both sides of every buffer)."""
     ckv, kpe = _cache(7, 4, 50 + 9)
     keep = np.tile(np.arange(9, dtype=np.int32), (4, 1))
     keep[0, :3] = [0, 3, 4]   # stream 0: valid
@@ -90,10 +93,17 @@ def test_invalid_keep_is_flagged_and_stream_untouched(lib):
     keep[1, :3] = [0, 4, 4]   # not strictly increasing
     keep[2, :3] = [0, 2, 99]  # beyond the cache
     # stream 3: n_keep larger than the keep row
-    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    gc, gk = run_compact(lib, ckv, kpe, 50, keep, n_keep, status)
-    assert int(status.item()) & lib.STATUS_BAD_KEEP
+    c, k = guarded_bf16(ckv), guarded_bf16(kpe)
+    gkeep, gn = guarded_i32(keep), guarded_i32(n_keep)
+    status = Guarded((1,), torch.int32, fill=0)
+    lib.compact_kv(c.t, k.t, 50, gkeep.t, gn.t, status=status.t)
+    torch.cuda.synchronize()
+    gc, gk = host_bits(c.t), host_bits(k.t)
+    assert int(status.t.item()) & lib.STATUS_BAD_KEEP
     rc, rk = oracle.compact_kv(ckv[:1], kpe[:1], 50, keep[:1], n_keep[:1])
     assert np.array_equal(gc[0], rc[0]) and np.array_equal(gk[0], rk[0])
     for s in (1, 2, 3):
         assert np.array_equal(gc[s], ckv[s]) and np.array_equal(gk[s], kpe[s])
+    assert np.array_equal(gkeep.t.cpu().numpy(), keep) and np.array_equal(gn.t.cpu().numpy(), n_keep)
+    for g in (c, k, gkeep, gn, status):
+        assert g.intact(), "write outside a buffer"

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import dev_bf16, dev_i32, host_bits
+from gpu_util import Guarded, guarded_bf16, dev_bf16, dev_i32, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -108,6 +108,8 @@ def test_compact_kv_layers(lib):
 
 
 def test_compact_kv_layers_bad_keep(lib):
+    """Invalid keep rows are flagged and skipped in every layer; nothing is written outside the
+    layers' caches or the status word (guard bands of canary bytes around each)."""
     q, n_layers, prefix = 9, 4, 50
     parents, _, _ = trees(91, 3, q)
     keep = np.array([[0, 2, 5, -1, -1, -1, -1, -1, -1],
@@ -115,12 +117,14 @@ def test_compact_kv_layers_bad_keep(lib):
                      [0, 1, 2, 3, 4, 5, 6, 7, 8]], np.int32)
     n_keep = np.array([3, 3, 10], np.int32)              # stream 2: more than keep_stride
     host = synth.layer_caches(92, n_layers, 3, prefix + q)
-    dev = upload(host)
-    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    lib.compact_kv_layers(dev, prefix, dev_i32(keep), dev_i32(n_keep), status=status)
+    guarded = [(guarded_bf16(c), guarded_bf16(k)) for c, k in host]
+    dev = [(c.t, k.t) for c, k in guarded]
+    status = Guarded((1,), torch.int32, fill=0)
+    lib.compact_kv_layers(dev, prefix, dev_i32(keep), dev_i32(n_keep), status=status.t)
     torch.cuda.synchronize()
-    assert status.item() == 2
+    assert status.t.item() == 2
     check_layers(dev, host, [prefix] * 3, keep, np.array([3, 0, 0], np.int32), "bad keep")
+    assert status.intact() and all(c.intact() and k.intact() for c, k in guarded), "write outside a buffer"
 
 
 def test_one_layer_equals_single_cache_call(lib):

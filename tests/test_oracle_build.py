@@ -144,6 +144,22 @@ def test_sibling_weight_evaluated_in_the_pages_order():
     assert int(t["logw"][idx[0]:idx[0] + 1].view(np.uint32)[0]) == 0xC03F5C2A
 
 
+def test_signed_zero_weights_tie():
+    """-0.0 and +0.0 are equal weights, so they pop in insertion order.  With
+    lp = [[-0, +0, -0], [-0, +0, -0]] (IEEE sums, round to nearest):
+      pop 1: (depth 1, rank 0) w = -0; offers its sibling (-0 - -0) + +0 = +0 (insertion 1)
+             and its child -0 + -0 = -0 (insertion 2);
+      pop 2: insertion 1 (w = +0); offers (+0 - +0) + -0 = +0 and +0 + -0 = +0 (insertions 3, 4);
+      pop 3: insertion 2, the depth-2 child of node 1, weight -0 -- ahead of the later +0
+             candidates although an order that puts +0 above -0 would take insertion 3."""
+    lp = np.array([[-0.0, 0.0, -0.0], [-0.0, 0.0, -0.0]], np.float32)
+    tok = np.arange(6, dtype=np.int32).reshape(2, 3)
+    t = ob.tree_build(lp, tok, 3)
+    assert t["parents"].tolist() == [-1, 0, 0, 1]
+    assert t["depths"].tolist() == [0, 1, 1, 2] and t["ranks"].tolist() == [0, 0, 1, 0]
+    assert np.signbit(t["logw"]).tolist() == [False, True, False, True]
+
+
 def test_rejects_budget_out_of_range():
     lp, tok = synth.drafter_topk(1, 0, 3, 2)
     for b in (0, 64):

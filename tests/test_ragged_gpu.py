@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import assert_close, dev_bf16, dev_i32, host_bits
+from gpu_util import Guarded, assert_close, dev_bf16, dev_i32, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -82,17 +82,32 @@ def test_long_prefixes(lib):
 
 
 def test_bad_prefixes_are_poisoned_and_flagged(lib):
+    """Out-of-range prefix entries poison their streams and set the status bit; the neighbours
+    are right; nothing is written outside out_lat, lse, the workspace and the status word (guard
+    bands of canary bytes around each), with the automatic plan and with forced splits."""
     prefixes = [5, -1, 2000, 7]
     q, max_p = 9, 1024
     b = ragged_batch(10, [5, 0, max_p, 7], q)
-    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    out, lse = run_ragged(lib, b, prefixes, max_p, 0, status)
-    assert status.item() & 4
-    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
-    assert np.isnan(out[2]).all() and np.isnan(lse[2]).all()
-    ro, rl = oracle.verify_attn_ragged(b.q_lat[[0, 3]], b.q_pe[[0, 3]], b.ckv[[0, 3]], b.kpe[[0, 3]], [5, 7],
-                                       b.parents[[0, 3]])
-    assert_close(out[[0, 3]], lse[[0, 3]], ro, rl, "good streams beside bad ones")
+    for splits in (0, 4):
+        out = Guarded((4, q, 64, 512), torch.float32)
+        lse = Guarded((4, q, 64), torch.float32)
+        status = Guarded((1,), torch.int32, fill=0)
+        need = lib.workspace_size(max_p, q, 4, splits)
+        ws = Guarded((need,), torch.uint8) if need else None
+        lib.verify_attn_ragged(dev_bf16(b.q_lat), dev_bf16(b.q_pe), dev_bf16(b.ckv), dev_bf16(b.kpe),
+                               dev_i32(np.array(prefixes)), max_p, dev_i32(b.parents), out=out.t, lse=lse.t,
+                               num_splits=splits, workspace=None if ws is None else ws.t, status=status.t)
+        torch.cuda.synchronize()
+        o, l = out.t.cpu().numpy(), lse.t.cpu().numpy()
+        assert status.t.item() & 4
+        assert np.isnan(o[1]).all() and np.isnan(l[1]).all()
+        assert np.isnan(o[2]).all() and np.isnan(l[2]).all()
+        ro, rl = oracle.verify_attn_ragged(b.q_lat[[0, 3]], b.q_pe[[0, 3]], b.ckv[[0, 3]], b.kpe[[0, 3]], [5, 7],
+                                           b.parents[[0, 3]])
+        assert_close(o[[0, 3]], l[[0, 3]], ro, rl, "good streams beside bad ones")
+        for g in (out, lse, status) + ((ws,) if ws is not None else ()):
+            assert g.intact(), f"write outside a buffer (splits={splits})"
+        assert splits == 0 or need > 0
 
 
 def test_compact_ragged(lib):

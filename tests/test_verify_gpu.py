@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import assert_close, dev_bf16, dev_i32
+from gpu_util import Guarded, assert_close, dev_bf16, dev_i32
 
 pytestmark = pytest.mark.gpu
 
@@ -76,12 +76,13 @@ def test_workloads_full(lib, name):
     check(lib, b, w.prefix, splits=0, what=name)
 
 
-def test_headline_workload_sampled_streams(lib):
+def test_headline_workload_all_streams(lib):
     """The 64-stream, prefix-4096, q_len-33 launch exactly as the benchmark runs it (automatic
-    split choice); eight streams spread over the batch are checked element by element."""
+    split choice, per-XCD block renumbering, part of the odd node's workgroups dispatched ahead
+    of the pairs, split merge): every one of the 64 streams is checked element by element."""
     w = synth.WORKLOADS[synth.HEADLINE]
     b = synth.make_batch(w)
-    check(lib, b, w.prefix, splits=0, streams=[0, 9, 18, 27, 36, 45, 54, 63], what=w.name)
+    check(lib, b, w.prefix, splits=0, what=w.name)
 
 
 def test_plain_entry_matches_ex(lib):
@@ -159,17 +160,54 @@ def test_kv_row_stride_larger_than_needed(lib):
 
 def test_malformed_parents_flag_status_and_stay_in_bounds(lib):
     """A bad parents[] entry sets the status bit; the walk stops there; the other streams are
-    unaffected."""
+    unaffected; nothing is written outside out_lat, lse, the workspace and the status word
+    (guard bands of canary bytes on both sides of each), with and without key splits."""
     b = synth.random_inputs(45, 3, 100, 9)
     bad = b.parents.copy()
     bad[1, 5] = 7  # not an earlier node
     bad[1, 0] = 3  # root must be -1
-    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    out, lse = lib.verify_attn_ex(dev_bf16(b.q_lat), dev_bf16(b.q_pe), dev_bf16(b.ckv), dev_bf16(b.kpe), 100,
-                                  dev_i32(bad), status=status, num_splits=1)
-    torch.cuda.synchronize()
-    assert int(status.item()) & lib.STATUS_BAD_PARENTS
-    ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, 100, b.parents, streams=[0, 2])
-    o, l = out.cpu().numpy(), lse.cpu().numpy()
-    assert_close(o[[0, 2]], l[[0, 2]], ro, rl, "good streams beside a bad one")
-    assert np.isfinite(o).all()
+    for splits in (1, 3):
+        out = Guarded((3, 9, 64, 512), torch.float32)
+        lse = Guarded((3, 9, 64), torch.float32)
+        status = Guarded((1,), torch.int32, fill=0)
+        need = lib.workspace_size(100, 9, 3, splits)
+        ws = Guarded((max(need, 1),), torch.uint8) if need else None
+        lib.verify_attn_ex(dev_bf16(b.q_lat), dev_bf16(b.q_pe), dev_bf16(b.ckv), dev_bf16(b.kpe), 100,
+                           dev_i32(bad), out=out.t, lse=lse.t, status=status.t, num_splits=splits,
+                           workspace=None if ws is None else ws.t)
+        torch.cuda.synchronize()
+        assert int(status.t.item()) & lib.STATUS_BAD_PARENTS
+        ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, 100, b.parents, streams=[0, 2])
+        o, l = out.t.cpu().numpy(), lse.t.cpu().numpy()
+        assert_close(o[[0, 2]], l[[0, 2]], ro, rl, "good streams beside a bad one")
+        assert np.isfinite(o).all()
+        for g in (out, lse, status) + ((ws,) if ws is not None else ()):
+            assert g.intact(), f"write outside a buffer (splits={splits})"
+        assert splits == 1 or need > 0
+
+
+def test_low_side_second_pass_from_a_fully_masked_first_tile(lib):
+    """The reference max of a split is taken from its first tile; when that tile is fully masked
+    for a node, the reference is 0 and every visible score of the node can sit far below it.
+    P = 48, q_len 64, two splits of two 32-key tiles: split 1 holds tree nodes 16..63, and its
+    first tile (nodes 16..47) is fully masked for node 50, a child of the root.  All scores are
+    near -295 (natural log), the node's own row near -259, so exponentials against a reference of
+    0 underflow: only the exact-max second pass gives the right split partial, and since node
+    50's own row dominates its softmax, that partial decides the output."""
+    b = synth.random_inputs(46, 1, 48, 64)
+    par = b.parents[0]
+    par[50] = 0
+    for j in range(51, 64):  # nobody descends from 50, so only node 50 sees its row
+        if par[j] == 50:
+            par[j] = 0
+    qpe = np.full(b.q_pe.shape, 8.0, np.float32)
+    kpe = np.full(b.kpe.shape, -8.0, np.float32)
+    kpe[0, 48 + 50] = -7.0
+    b.q_pe[:] = synth.f32_to_bf16_bits(qpe)
+    b.kpe[:] = synth.f32_to_bf16_bits(kpe)
+    assert lib.num_splits(48, 64, 1, 2) == 2
+    out, lse = run(lib, b, 48, splits=2)
+    ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, 48, b.parents)
+    assert -270 < rl[0, 50].max() < -250 and rl[0, 50].min() > -270  # node 50's own row dominates
+    assert rl.max() < -200
+    assert_close(out, lse, ro, rl, "low-side second pass")

@@ -28,8 +28,10 @@ constexpr int kBuildMaxD = 64;
 constexpr int kBuildMaxK = 64;
 
 // float -> uint32 with the same order (finite values; larger float, larger key, never 0).
+// -0.0 takes +0.0's key: the two compare equal, so their order is the insertion order.
 __device__ __forceinline__ unsigned ordered_key(float w) {
-  const unsigned u = __float_as_uint(w);
+  unsigned u = __float_as_uint(w);
+  if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

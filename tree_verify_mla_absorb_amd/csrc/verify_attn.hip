@@ -578,7 +578,10 @@ verify_attn_kernel(VerifyArgs a) {
       ++t;
       for (; t < t_mask; ++t) step(t, Flag<false>{}, Flag<false>{}, Flag<false>{}, half_tag);
       for (; t < t_end; ++t) step(t, Flag<true>{}, Flag<false>{}, Flag<false>{}, half_tag);
-      // last tile's values
+      // last tile's values.  The last step issued its 9 staging instructions against empty
+      // resources; out-of-range lanes of an LDS load still write zeros into their stage, which
+      // the output transpose areas overlap, so every wave waits for them before the barrier.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
       {
         const int last_stg = (t_end - 1 - t_begin) % kStages, last_pbuf = (t_end - 1 - t_begin) & 1;
