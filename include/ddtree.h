@@ -125,6 +125,26 @@ int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, 
                           void* workspace, size_t workspace_bytes, int32_t* dev_status,
                           hipStream_t stream);
 
+/*
+ * ddtree_verify_attn_noalloc -- ddtree_verify_attn_ex without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The call itself allocates nothing: the split partials go
+ * to a scratch array inside the library, DDTREE_NOALLOC_SCRATCH_BYTES on every GPU the library
+ * runs on, held until the process ends.
+ *   num_splits  0 = the best automatic plan whose partials fit in the scratch array (the
+ *               unsplit plan needs none); a forced count (n >= 1) whose partials do not fit
+ *               returns DDTREE_ERR_WORKSPACE (ddtree_verify_attn_workspace_size gives the bytes).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents: calls
+ * that can overlap on one GPU (issued to different streams without ordering) race and must not
+ * be made.  All other arguments, results and errors are those of ddtree_verify_attn_ex, plus
+ * DDTREE_ERR_HIP when the array's device address cannot be obtained.
+ */
+#define DDTREE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ddtree_verify_attn_noalloc(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
+                               int prefix_len, const int32_t* parents, int q_len, int n_streams,
+                               float* out_lat, float* lse, int kv_rows, float scale, int num_splits,
+                               int32_t* dev_status, hipStream_t stream);
+
 /* Bytes of workspace ddtree_verify_attn_ex needs for these arguments (0 when no split is
  * used).  Returns 0 for invalid sizes as well; the launch call then reports the error. */
 size_t ddtree_verify_attn_workspace_size(int prefix_len, int q_len, int n_streams,

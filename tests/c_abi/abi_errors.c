@@ -102,6 +102,18 @@ int main(void) {
   expect("num splits, forced 8", ddtree_verify_attn_num_splits(4096, 33, 1, 8), 8);
   expect("num splits, bad shape", ddtree_verify_attn_num_splits(16, 65, 1, 0), DDTREE_ERR_SHAPE);
 
+  /* ddtree_verify_attn_noalloc: validated like the _ex call; a forced plan whose partials do not
+     fit the library's scratch array is refused before anything is launched */
+  expect("noalloc NULL parents",
+         ddtree_verify_attn_noalloc(q_lat, q_pe, ckv, kpe, 16, NULL, 9, 1, out, lse, 25, 0.f, 0, status, stream),
+         DDTREE_ERR_NULL);
+  expect("noalloc forced plan beyond the scratch",
+         ddtree_verify_attn_workspace_size(4096, 33, 64, 64) > DDTREE_NOALLOC_SCRATCH_BYTES, 1);
+  expect("noalloc refuses it",
+         ddtree_verify_attn_noalloc(q_lat, q_pe, ckv, kpe, 4096, parents, 33, 64, out, lse, 4129, 0.f, 64, status,
+                                    stream),
+         DDTREE_ERR_WORKSPACE);
+
   /* ddtree_verify_attn_ragged */
   expect("ragged NULL prefix_lens",
          ddtree_verify_attn_ragged(q_lat, q_pe, ckv, kpe, NULL, 16, parents, 9, 1, out, lse, 25, 0.f, 1, NULL, 0,

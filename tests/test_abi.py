@@ -293,3 +293,20 @@ def test_automatic_split_plan_on_the_five_workloads():
     assert _lib.workspace_size(4096, 33, 1, 0) == ws(2048, 10, 64, 10)
     assert _lib.workspace_size(256, 9, 1, 0) == ws(512, 5, 64, 5)
     assert _lib.workspace_size(4096, 33, 64, 0) == ws(0, 1, 64 * 64, 4)
+
+
+def noalloc(q_lat=A, q_pe=B, ckv=C, kpe=D, prefix=100, parents=E, q=9, s=2, out=F, lse=G, splits=0, status=None):
+    return _lib.LIB.ddtree_verify_attn_noalloc(q_lat, q_pe, ckv, kpe, prefix, parents, q, s, out, lse, prefix + q,
+                                               0.0, splits, status, None)
+
+
+def test_noalloc_validation_before_any_launch():
+    m = re.search(r"#define DDTREE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+    assert noalloc(q_lat=None) == _lib.ERR_NULL
+    assert noalloc(q=65) == _lib.ERR_SHAPE
+    assert noalloc(ckv=C + 2) == _lib.ERR_ALIGN
+    assert noalloc(out=A) == _lib.ERR_ALIAS
+    # a forced split count whose partials exceed the scratch is refused on the host
+    assert _lib.workspace_size(4096, 33, 64, 64) > _lib.NOALLOC_SCRATCH_BYTES
+    assert noalloc(prefix=4096, q=33, s=64, splits=64) == _lib.ERR_WORKSPACE

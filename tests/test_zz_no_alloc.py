@@ -1,0 +1,76 @@
+"""ddtree_verify_attn_noalloc through the C ABI: the entry point for callers that cannot allocate
+keeps its split partials in the library's own scratch array.  Its outputs must equal those of
+ddtree_verify_attn_ex (same plan, same kernels: bitwise) and meet the oracle's bars, on two calls
+in a row (the second smaller, so it runs over the first call's leftovers in the scratch), with a
+plan that falls back to fit the scratch, and a forced split count too large for it is refused
+before anything is launched."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_close, dev_bf16, dev_i32
+
+pytestmark = pytest.mark.gpu
+
+
+def inputs(seed, s, p, q):
+    b = synth.random_inputs(seed, s, p, q)
+    return b, (dev_bf16(b.q_lat), dev_bf16(b.q_pe), dev_bf16(b.ckv), dev_bf16(b.kpe), dev_i32(b.parents))
+
+
+def both(lib, t, prefix, splits):
+    ql, qp, c, k, par = t
+    s, q = par.shape
+    o1 = torch.full((s, q, 64, 512), float("nan"), device="cuda:0")
+    l1 = torch.full((s, q, 64), float("nan"), device="cuda:0")
+    o2, l2 = torch.full_like(o1, float("nan")), torch.full_like(l1, float("nan"))
+    lib.verify_attn_ex(ql, qp, c, k, prefix, par, out=o1, lse=l1, num_splits=splits)
+    lib.verify_attn_noalloc(ql, qp, c, k, prefix, par, out=o2, lse=l2, num_splits=splits)
+    torch.cuda.synchronize()
+    return o1.cpu().numpy(), l1.cpu().numpy(), o2.cpu().numpy(), l2.cpu().numpy()
+
+
+def test_noalloc_matches_ex_on_two_calls_in_a_row(lib):
+    # first call: 2 streams, prefix 4096, q_len 33, automatic plan (7 splits: partials in the scratch)
+    print("[noalloc] S=2 P=4096 Q=33 auto", flush=True)
+    assert lib.num_splits(4096, 33, 2, 0) > 1 and 0 < lib.workspace_size(4096, 33, 2, 0) <= lib.NOALLOC_SCRATCH_BYTES
+    b, t = inputs(61, 2, 4096, 33)
+    o1, l1, o2, l2 = both(lib, t, 4096, 0)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)) and np.array_equal(l1.view(np.uint32),
+                                                                                     l2.view(np.uint32))
+    ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, 4096, b.parents)
+    assert_close(o2, l2, ro, rl, "noalloc, first call")
+    # second call, smaller: 1 stream, prefix 300, q_len 9, 3 forced splits
+    print("[noalloc] S=1 P=300 Q=9 splits=3", flush=True)
+    b, t = inputs(62, 1, 300, 9)
+    o1, l1, o2, l2 = both(lib, t, 300, 3)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)) and np.array_equal(l1.view(np.uint32),
+                                                                                     l2.view(np.uint32))
+    ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, 300, b.parents)
+    assert_close(o2, l2, ro, rl, "noalloc, second call")
+
+
+def test_noalloc_plan_falls_back_to_fit_the_scratch(lib):
+    # the automatic plan of ddtree_verify_attn_ex needs more than the scratch holds here
+    print("[noalloc] S=2 P=4096 Q=64 auto (fallback plan)", flush=True)
+    assert lib.workspace_size(4096, 64, 2, 0) > lib.NOALLOC_SCRATCH_BYTES
+    b, (ql, qp, c, k, par) = inputs(63, 2, 4096, 64)
+    out, lse = lib.verify_attn_noalloc(ql, qp, c, k, 4096, par)
+    torch.cuda.synchronize()
+    ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, 4096, b.parents)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "noalloc fallback plan")
+
+
+def test_noalloc_refuses_a_forced_plan_larger_than_the_scratch(lib):
+    s, p, q = 64, 4096, 33
+    assert lib.workspace_size(p, q, s, 64) > lib.NOALLOC_SCRATCH_BYTES
+    ql = torch.empty((s, q, 64, 512), dtype=torch.bfloat16, device="cuda:0")
+    qp = torch.empty((s, q, 64, 64), dtype=torch.bfloat16, device="cuda:0")
+    c = torch.empty((s, p + q, 512), dtype=torch.bfloat16, device="cuda:0")
+    k = torch.empty((s, p + q, 64), dtype=torch.bfloat16, device="cuda:0")
+    par = torch.zeros((s, q), dtype=torch.int32, device="cuda:0")
+    with pytest.raises(lib.DDTreeError) as e:
+        lib.verify_attn_noalloc(ql, qp, c, k, p, par, num_splits=64)
+    assert e.value.code == lib.ERR_WORKSPACE

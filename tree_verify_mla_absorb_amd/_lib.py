@@ -18,6 +18,7 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = -1, -2, -3, -4, -5, -6
 STATUS_BAD_PARENTS, STATUS_BAD_KEEP, STATUS_BAD_PREFIX, STATUS_BAD_POSITION = 1, 2, 4, 8
 HEADS, D_LATENT, D_ROPE, MAX_Q_LEN, MAX_LAYERS = 64, 512, 64, 64, 128
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DDTREE_NOALLOC_SCRATCH_BYTES
 
 
 def _load() -> ctypes.CDLL:
@@ -30,6 +31,8 @@ def _load() -> ctypes.CDLL:
     lib.ddtree_verify_attn_ex.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, i32, f32, i32, vp, sz,
                                           vp, vp]
     lib.ddtree_verify_attn_ex.restype = i32
+    lib.ddtree_verify_attn_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, i32, f32, i32, vp, vp]
+    lib.ddtree_verify_attn_noalloc.restype = i32
     lib.ddtree_verify_attn_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.ddtree_verify_attn_workspace_size.restype = sz
     lib.ddtree_verify_attn_num_splits.argtypes = [i32, i32, i32, i32]
@@ -67,6 +70,7 @@ LIB = _load()
 EXPORTED = (
     "ddtree_verify_attn",
     "ddtree_verify_attn_ex",
+    "ddtree_verify_attn_noalloc",
     "ddtree_verify_attn_workspace_size",
     "ddtree_verify_attn_num_splits",
     "ddtree_compact_kv",
@@ -192,6 +196,20 @@ def verify_attn_ex(q_lat, q_pe, ckv, kpe, prefix_len: int, parents, *, out=None,
     _check(LIB.ddtree_verify_attn_ex(_ptr(q_lat), _ptr(q_pe), _ptr(ckv), _ptr(kpe), int(prefix_len), _ptr(parents),
                                      int(q), int(s), _ptr(out), _ptr(lse), int(rows), float(scale),
                                      int(num_splits), _ptr(workspace), nbytes, _ptr(status), _stream(stream)))
+    return out, lse
+
+
+def verify_attn_noalloc(q_lat, q_pe, ckv, kpe, prefix_len: int, parents, *, out=None, lse=None, scale: float = 0.0,
+                        num_splits: int = 0, status=None, stream=None):
+    """``ddtree_verify_attn_noalloc``: ``verify_attn_ex`` with the split partials in the library's
+    own scratch array (no workspace)."""
+    s, q, rows = _shapes(q_lat, q_pe, ckv, kpe, parents)
+    out, lse = _outputs(q_lat, out, lse)
+    if status is not None:
+        _need(status, "status", (torch.int32,))
+    _check(LIB.ddtree_verify_attn_noalloc(_ptr(q_lat), _ptr(q_pe), _ptr(ckv), _ptr(kpe), int(prefix_len),
+                                          _ptr(parents), int(q), int(s), _ptr(out), _ptr(lse), int(rows),
+                                          float(scale), int(num_splits), _ptr(status), _stream(stream)))
     return out, lse
 
 

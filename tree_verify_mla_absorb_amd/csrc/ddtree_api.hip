@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/ddtree.h"
 #include "kernels.h"
@@ -98,7 +99,19 @@ double plan_cost(const Plan& p, long long units0, long long units1, int cus) {
   return t;
 }
 
-Plan make_plan(int prefix_len, int q_len, int n_streams, int num_splits) {
+// Workgroup counts and partial rows of a plan whose split counts are set.
+void finish_plan(Plan& p, long long units0, long long units1) {
+  p.wgs[0] = units0 * p.splits[0];
+  p.wgs[1] = units1 * p.splits[1];
+  p.part_rows[0] = units0 * 2 * kHeads;
+  p.part_rows[1] = units1 * kHeads;
+}
+
+size_t workspace_bytes_for(const Plan& p);
+
+// The split plan for these sizes.  An automatic plan (num_splits == 0) only considers plans
+// whose partials fit in ws_cap bytes (the unsplit plan needs none, so one always fits).
+Plan make_plan(int prefix_len, int q_len, int n_streams, int num_splits, size_t ws_cap = (size_t)-1) {
   Plan p;
   p.n_pairs = q_len / 2;
   p.has_odd = q_len & 1;
@@ -125,6 +138,8 @@ Plan make_plan(int prefix_len, int q_len, int n_streams, int num_splits) {
         const int s1 = cand[ci];
         if (units1 == 0 && s1 > 1) break;
         set_splits(trial, 1, s1);
+        finish_plan(trial, units0, units1);
+        if (workspace_bytes_for(trial) > ws_cap) continue;
         const double c = plan_cost(trial, units0, units1, cus);
         if (c < best - 1e-9) {
           best = c;
@@ -138,10 +153,7 @@ Plan make_plan(int prefix_len, int q_len, int n_streams, int num_splits) {
   }
   if (p.tiles_per_split[0] == 0) set_splits(p, 0, 1);
   if (p.tiles_per_split[1] == 0) set_splits(p, 1, 1);
-  p.wgs[0] = units0 * p.splits[0];
-  p.wgs[1] = units1 * p.splits[1];
-  p.part_rows[0] = units0 * 2 * kHeads;
-  p.part_rows[1] = units1 * kHeads;
+  finish_plan(p, units0, units1);
   return p;
 }
 
@@ -197,12 +209,39 @@ size_t ddtree_verify_attn_workspace_size(int prefix_len, int q_len, int n_stream
 
 namespace {
 
+// Split partials of ddtree_verify_attn_noalloc, for callers that cannot allocate: one array per
+// GPU, held until the process ends.  Host code never passes the array's name to a kernel (on the
+// host it only stands in for the symbol); it passes the device address that hipGetSymbolAddress
+// reports for the current GPU, looked up once per device.
+constexpr size_t kScratchBytes = DDTREE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {};
+
+// The current GPU's scratch address, or an error code.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DDTREE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DDTREE_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return DDTREE_OK;
+}
+
 // ddtree_verify_attn_ex and ddtree_verify_attn_ragged: prefix_lens == nullptr means every stream
 // has prefix_len rows of prefix; otherwise prefix_len bounds the per-stream device values.
+// use_scratch (ddtree_verify_attn_noalloc): the partials go to this GPU's scratch array instead
+// of a caller workspace, and the plan is restricted to partials that fit there.
 int verify_impl(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe, int prefix_len,
                 const int32_t* prefix_lens, const int32_t* parents, int q_len, int n_streams, float* out_lat,
                 float* lse, int kv_rows, float scale, int num_splits, void* workspace, size_t workspace_bytes,
-                int32_t* dev_status, hipStream_t stream) {
+                int32_t* dev_status, hipStream_t stream, bool use_scratch = false) {
   if (!q_lat || !q_pe || !ckv || !kpe || !parents || !out_lat || !lse) return DDTREE_ERR_NULL;
   if (!shape_ok(prefix_len, q_len, n_streams) || num_splits < 0) return DDTREE_ERR_SHAPE;
   if (kv_rows < prefix_len + q_len) return DDTREE_ERR_SHAPE;
@@ -226,7 +265,7 @@ int verify_impl(const void* q_lat, const void* q_pe, const void* ckv, const void
     if (overlap(in, r_out) || overlap(in, r_lse)) return DDTREE_ERR_ALIAS;
   if (overlap(r_out, r_lse)) return DDTREE_ERR_ALIAS;
 
-  const Plan plan = make_plan(prefix_len, q_len, n_streams, num_splits);
+  const Plan plan = make_plan(prefix_len, q_len, n_streams, num_splits, use_scratch ? kScratchBytes : (size_t)-1);
   const long long blocks = plan.wgs[0] + plan.wgs[1];
   if (blocks > kMaxGrid) return DDTREE_ERR_SHAPE;
 
@@ -257,6 +296,16 @@ int verify_impl(const void* q_lat, const void* q_pe, const void* ckv, const void
   a.scale_log2e = scale * 1.4426950408889634f;
 
   const size_t need = workspace_bytes_for(plan);
+  if (use_scratch) {
+    if (need > kScratchBytes) return DDTREE_ERR_WORKSPACE;  // a forced split count too large
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      const int rc = scratch_address(&workspace);
+      if (rc != DDTREE_OK) return rc;
+      workspace_bytes = kScratchBytes;
+    }
+  }
   if (need > 0) {
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DDTREE_ERR_WORKSPACE;
     const Range r_ws = range_of(workspace, need);
@@ -310,6 +359,14 @@ int ddtree_verify_attn_ragged(const void* q_lat, const void* q_pe, const void* c
   if (!prefix_lens) return DDTREE_ERR_NULL;
   return verify_impl(q_lat, q_pe, ckv, kpe, max_prefix_len, prefix_lens, parents, q_len, n_streams, out_lat, lse,
                      kv_rows, scale, num_splits, workspace, workspace_bytes, dev_status, stream);
+}
+
+int ddtree_verify_attn_noalloc(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
+                               int prefix_len, const int32_t* parents, int q_len, int n_streams, float* out_lat,
+                               float* lse, int kv_rows, float scale, int num_splits, int32_t* dev_status,
+                               hipStream_t stream) {
+  return verify_impl(q_lat, q_pe, ckv, kpe, prefix_len, nullptr, parents, q_len, n_streams, out_lat, lse, kv_rows,
+                     scale, num_splits, nullptr, 0, dev_status, stream, true);
 }
 
 int ddtree_verify_attn(const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
