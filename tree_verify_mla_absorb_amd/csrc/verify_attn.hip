@@ -45,6 +45,7 @@ namespace ddtree {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
@@ -328,7 +329,13 @@ verify_attn_kernel(VerifyArgs a) {
 
   f32x16 o[4][4];        // [head block][32-dim block]: dims 128 wave + 32 db + 8 (i / 4) + 4 g + i % 4
   float m_ref = 0.f;     // reference max (log2 units) of this lane's head, equal in both halves
-  float l_run = 0.f;     // this lane's share of the denominator
+  // This lane's share of the denominator, summed over the bf16-rounded probabilities that the
+  // value product multiplies: out = sum p~ v / sum p~ is then a convex combination of the value
+  // rows, and a row dominated by one key reproduces that key's row whatever its probability
+  // rounded to.  (An fp32 sum of the unrounded probabilities leaves that rounding, up to 2^-8
+  // relative, in the output.)  lse takes the same sum, within 2^-8 relative of the exact one,
+  // i.e. within 0.004 in natural-log units.
+  float l_run = 0.f;
   float mx_run = -INFINITY;
   const float cs = a.scale_log2e;
   // This split's tiles of this stream (a split past a short stream's end is empty: it writes
@@ -372,6 +379,7 @@ verify_attn_kernel(VerifyArgs a) {
 #pragma unroll
     for (int u = kKAhead; u < 4; ++u) qb[u] = qpe_frag(u);
     f32x16 st;
+    bf16x8 kprev, qprev;
 #pragma unroll
     for (int u = 0; u < 36; ++u) {
       const bf16x8 kcur = kb[u % kKAhead];
@@ -380,14 +388,27 @@ verify_attn_kernel(VerifyArgs a) {
       if (u % kDmaEvery == 1 && u / kDmaEvery < kDmaInScores) dma(u / kDmaEvery);
       if (u == kHookStep) hook();
       score_step(st, kcur, qcur, u);
+      // The compiler cannot see inside the asm MFMA, so it would treat the operand registers as
+      // free once the asm is issued.  They stay in use until the next MFMA of the chain has
+      // issued -- and that one waits for this one's result, so by then every operand read is
+      // done -- and no later write (VALU or LDS) can reach them while the matrix core reads them.
+      if (u > 0) asm volatile("" ::"v"(kprev), "v"(qprev));
+      kprev = kcur;
+      qprev = qcur;
       __builtin_amdgcn_sched_barrier(0);
     }
+    asm volatile("" ::"v"(kprev), "v"(qprev));
     return st;
   };
 
+  // ---- running sum plus rounded probabilities e, e + 1 (e even) of a tile
+  auto sum_pair = [](const bf16x8 (&pb)[2], int e, float sum) __attribute__((always_inline)) -> float {
+    const bf16x2 pr = {pb[e >> 3][e & 7], pb[e >> 3][(e & 7) + 1]};
+    return __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, sum, false);
+  };
   // ---- probabilities of accumulator entries 2 k, 2 k + 1 of tile t (entry i holds key
   //      8 (i / 4) + 4 g + i % 4 of the tile): visibility, running raw max, exp2 against the
-  //      reference, running sum, bf16 packing.
+  //      reference, bf16 packing, and the running sum of the rounded probabilities.
   auto prob_pair = [&](const f32x16& st, int t, int k, auto masked_tag, bf16x8 (&pb)[2], float& psum,
                        float& mx) __attribute__((always_inline)) {
     constexpr bool kMasked = decltype(masked_tag)::value;
@@ -402,9 +423,12 @@ verify_attn_kernel(VerifyArgs a) {
       }
       mx = fmaxf(mx, x);
       const float pv = __builtin_amdgcn_exp2f(fmaf(x, cs, -m_ref));
-      psum += pv;
       pb[e >> 3][e & 7] = (__bf16)pv;
     }
+    // The previous rounded pair joins the sum (one dot2 with (1, 1)).  One pair late, so that
+    // it never waits for this pair's exponentials and packing; the last pair of the tile is
+    // added by the caller.
+    if (k > 0) psum = sum_pair(pb, 2 * k - 2, psum);
   };
   auto publish = [&](int pbuf, int u, const bf16x8& v) __attribute__((always_inline)) {
     *reinterpret_cast<bf16x8*>(smem + kPOff + pbuf * kPBytes + wave * 2048 + lane16 + u * 1024) = v;
@@ -517,6 +541,7 @@ verify_attn_kernel(VerifyArgs a) {
           },
           half_tag);
     }
+    psum = sum_pair(pb, 14, psum);
     l_run += psum;
     mx_run = fmaxf(mx_run, mx * cs);
   };
