@@ -102,8 +102,16 @@ constexpr int kStageInstrs = kTileKeys / 4 + 1;
 // k-steps); the rest go into the first value steps.
 constexpr int kDmaEvery = 5;
 constexpr int kDmaInScores = 7;
-// Score k-step at which the first reads of the following value product are issued.
-constexpr int kHookStep = 34;
+// In a one-node workgroup the two waves of a head block split its score chain: waves 0, 1 take
+// the 4 rotary and the first 14 latent k-steps, waves 2, 3 the last 18 latent ones, and the
+// halves meet through LDS.  A half chain carries a staging instruction every kDmaEveryHalf
+// k-steps, kDmaInHalf of them.
+constexpr int kSplitStep = 18;
+constexpr int kDmaEveryHalf = 3;
+constexpr int kDmaInHalf = 6;
+// s_waitcnt immediate for lgkmcnt(0) alone (vmcnt and expcnt at their maximum): the exchange
+// barrier waits for this wave's LDS writes, not for the staging in flight.
+constexpr int kWaitLgkmcnt0 = 0xC07F;
 // Value step that reads the probabilities of the second 16-key slice.
 constexpr int kP1Step = 3;
 
@@ -139,10 +147,10 @@ __device__ __forceinline__ void dma16(unsigned lds_addr, i32x4 rsrc, int voff, i
 // matrix core forwards back to back); the first step starts from 0.  The last step ends with
 // 18 wait states so that the VALU reads of the scores that follow see the final result
 // (an 8-pass XDL result needs 12 before a VALU read on gfx950).
-__device__ __forceinline__ void score_step(f32x16& st, const bf16x8& k, const bf16x8& q, int u) {
-  if (u == 0)
+__device__ __forceinline__ void score_step(f32x16& st, const bf16x8& k, const bf16x8& q, bool first, bool last) {
+  if (first)
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(st) : "v"(k), "v"(q));
-  else if (u == 35)
+  else if (last)
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 1"
                  : "+v"(st) : "v"(k), "v"(q));
   else
@@ -192,6 +200,11 @@ __device__ __forceinline__ int balanced_stream(const int32_t* prefix_lens, int n
 template <bool B>
 struct Flag {
   static constexpr bool value = B;
+};
+// k-steps [A, B) of the score chain
+template <int A, int B>
+struct Steps {
+  static constexpr int u0 = A, u1 = B;
 };
 
 __global__ void __attribute__((amdgpu_flat_work_group_size(kWGThreads, kWGThreads),
@@ -352,8 +365,12 @@ verify_attn_kernel(VerifyArgs a) {
   bf16x8 qf[32];
 
 
-  // ---- S^T of a tile held in stage stg: 32 latent + 4 rotary k-steps
-  auto score_mma = [&](int stg, auto&& hook, auto&& dma) __attribute__((always_inline)) -> f32x16 {
+  // ---- S^T of a tile held in stage stg: 4 rotary + 32 latent k-steps (k-steps [U0, U1) of
+  //      them for a half chain)
+  auto score_mma = [&](int stg, auto&& hook, auto&& dma, auto steps_tag) __attribute__((always_inline)) -> f32x16 {
+    constexpr int U0 = decltype(steps_tag)::u0, U1 = decltype(steps_tag)::u1;
+    constexpr int kEvery = U1 - U0 == 36 ? kDmaEvery : kDmaEveryHalf;
+    constexpr int kIn = U1 - U0 == 36 ? kDmaInScores : kDmaInHalf;
     const unsigned char* st_base = smem + stg * kStageBytes;
     // k-step u: the 4 rotary k-steps first (both operands in LDS), then the 32 latent ones
     // (Q in registers).
@@ -372,27 +389,28 @@ verify_attn_kernel(VerifyArgs a) {
     // of the value product.
     bf16x8 kb[kKAhead], qb[4];
 #pragma unroll
-    for (int u = 0; u < kKAhead; ++u) {
-      kb[u] = kfrag(u);
+    for (int u = U0; u < U0 + kKAhead; ++u) {
+      kb[(u - U0) % kKAhead] = kfrag(u);
       if (u < 4) qb[u] = qpe_frag(u);
     }
 #pragma unroll
-    for (int u = kKAhead; u < 4; ++u) qb[u] = qpe_frag(u);
+    for (int u = U0 + kKAhead; u < 4; ++u) qb[u] = qpe_frag(u);
     f32x16 st;
     bf16x8 kprev, qprev;
 #pragma unroll
-    for (int u = 0; u < 36; ++u) {
-      const bf16x8 kcur = kb[u % kKAhead];
+    for (int u = U0; u < U1; ++u) {
+      const int v = u - U0;
+      const bf16x8 kcur = kb[v % kKAhead];
       const bf16x8 qcur = u < 4 ? qb[u] : qf[u - 4];
-      if (u + kKAhead < 36) kb[u % kKAhead] = kfrag(u + kKAhead);
-      if (u % kDmaEvery == 1 && u / kDmaEvery < kDmaInScores) dma(u / kDmaEvery);
-      if (u == kHookStep) hook();
-      score_step(st, kcur, qcur, u);
+      if (u + kKAhead < U1) kb[v % kKAhead] = kfrag(u + kKAhead);
+      if (v % kEvery == 1 && v / kEvery < kIn) dma(v / kEvery);
+      if (u == U1 - 2) hook();
+      score_step(st, kcur, qcur, u == U0, u == U1 - 1);
       // The compiler cannot see inside the asm MFMA, so it would treat the operand registers as
       // free once the asm is issued.  They stay in use until the next MFMA of the chain has
       // issued -- and that one waits for this one's result, so by then every operand read is
       // done -- and no later write (VALU or LDS) can reach them while the matrix core reads them.
-      if (u > 0) asm volatile("" ::"v"(kprev), "v"(qprev));
+      if (u > U0) asm volatile("" ::"v"(kprev), "v"(qprev));
       kprev = kcur;
       qprev = qcur;
       __builtin_amdgcn_sched_barrier(0);
@@ -489,6 +507,9 @@ verify_attn_kernel(VerifyArgs a) {
     constexpr bool kFirst = decltype(first_tag)::value;
     constexpr bool kSetRef = decltype(set_ref_tag)::value;
     constexpr bool kMasked = decltype(masked_tag)::value;
+    constexpr bool kHalf = decltype(half_tag)::value;
+    // staging instructions of the next tile issued inside the score chain
+    constexpr int kIn = kHalf ? kDmaInHalf : kDmaInScores;
     const int i = t - t_begin;
     const int stg = i % kStages;
     const int pbuf = i & 1;
@@ -500,14 +521,47 @@ verify_attn_kernel(VerifyArgs a) {
     bf16x8 p0[4], vf;
     const int prev_stg = (i + 2) % kStages, prev_pbuf = (i + 1) & 1;
     f32x16 st;
+    auto chain = [&](auto&& hook) __attribute__((always_inline)) {
+      if constexpr (!kHalf) {
+        st = score_mma(stg, hook, dma, Steps<0, 36>{});
+      } else {
+        // a one-node workgroup: waves w and w + 2 split head block w's chain, and wave w + 2
+        // hands its partial scores to wave w through LDS (its own rotary-query area, unused
+        // here), behind a barrier that waits for LDS writes only -- the next tile's staging
+        // stays in flight
+        if (wave < 2)
+          st = score_mma(stg, hook, dma, Steps<0, kSplitStep>{});
+        else
+          st = score_mma(stg, hook, dma, Steps<kSplitStep, 36>{});
+        F32x4* xb = reinterpret_cast<F32x4*>(smem + kQpeOff + (2 + (wave & 1)) * 4096) + lane;
+        if (wave >= 2) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) xb[i4 * 64] = F32x4{st[4 * i4], st[4 * i4 + 1], st[4 * i4 + 2], st[4 * i4 + 3]};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if (wave < 2) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const F32x4 x = xb[i4 * 64];
+            st[4 * i4] += x[0];
+            st[4 * i4 + 1] += x[1];
+            st[4 * i4 + 2] += x[2];
+            st[4 * i4 + 3] += x[3];
+          }
+        }
+      }
+    };
     if constexpr (kFirst) {
 #pragma unroll
-      for (int j = kDmaInScores; j < kStageInstrs; ++j) dma(j);  // no value steps to carry them
-      st = score_mma(stg, no_hook, dma);
+      for (int j = kIn; j < kStageInstrs; ++j) dma(j);  // no value steps to carry them
+      chain(no_hook);
+    } else {
+      chain([&]() __attribute__((always_inline)) { value_prologue(prev_stg, prev_pbuf, p0, vf, half_tag); });
     }
-    else
-      st = score_mma(
-          stg, [&]() __attribute__((always_inline)) { value_prologue(prev_stg, prev_pbuf, p0, vf, half_tag); }, dma);
+    // in a one-node workgroup only waves 0, 1 hold whole scores: the softmax is theirs
+    const bool soft = !kHalf || wave < 2;
     bf16x8 pb[2];
     float psum = 0.f, mx = -INFINITY;
     if constexpr (kFirst) {
@@ -527,23 +581,29 @@ verify_attn_kernel(VerifyArgs a) {
         const float m0 = half_max(m * cs);
         m_ref = m0 == -INFINITY ? 0.f : m0;
       }
+      if (soft) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) prob_pair(st, t, k, masked_tag, pb, psum, mx);
-      publish(pbuf, 0, pb[0]);
-      publish(pbuf, 1, pb[1]);
+        for (int k = 0; k < 8; ++k) prob_pair(st, t, k, masked_tag, pb, psum, mx);
+        publish(pbuf, 0, pb[0]);
+        publish(pbuf, 1, pb[1]);
+      }
     } else {
       values(
           prev_stg, prev_pbuf, p0, vf,
           [&](int k) __attribute__((always_inline)) {
-            if (k < kStageInstrs - kDmaInScores) dma(kDmaInScores + k);
-            prob_pair(st, t, k, masked_tag, pb, psum, mx);
-            if ((k & 3) == 3) publish(pbuf, k >> 2, pb[k >> 2]);
+            if (k < kStageInstrs - kIn) dma(kIn + k);
+            if (soft) {
+              prob_pair(st, t, k, masked_tag, pb, psum, mx);
+              if ((k & 3) == 3) publish(pbuf, k >> 2, pb[k >> 2]);
+            }
           },
           half_tag);
     }
-    psum = sum_pair(pb, 14, psum);
-    l_run += psum;
-    mx_run = fmaxf(mx_run, mx * cs);
+    if (soft) {
+      psum = sum_pair(pb, 14, psum);
+      l_run += psum;
+      mx_run = fmaxf(mx_run, mx * cs);
+    }
   };
 
 #pragma unroll
@@ -563,29 +623,30 @@ verify_attn_kernel(VerifyArgs a) {
       mx_run = -INFINITY;
 
       stage_tile(t_begin, 0);
-      if (attempt == 0 && active) {
+      if (attempt == 0) {
+        // Latent queries of this wave's head block, k-steps [ks0, ks1): all 32 for a node pair;
+        // in a one-node workgroup the first kSplitStep - 4 for waves 0, 1 and the rest for
+        // waves 2, 3 (each half of the score chain; qc = q0 there).
+        constexpr bool kHalf = decltype(half_tag)::value;
         const size_t qrow = ((size_t)s * Q + qc) * kHeads + head;
         const uint16_t* ql = a.q_lat + qrow * kDLat + g * 8;
+        const bool lo = !kHalf || wave < 2, hi = !kHalf || wave >= 2;
 #pragma unroll
-        for (int ks = 0; ks < 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(ql + ks * 16);
+        for (int ks = 0; ks < 32; ++ks) {
+          const bool need = ks < kSplitStep - 4 ? lo : hi;
+          qf[ks] = need ? *reinterpret_cast<const bf16x8*>(ql + ks * 16) : bf16x8{};
+        }
         // Consume every fragment here, so the wait for these loads happens once, before the key
         // loop: otherwise the loop's MFMAs carry waits that also drain the tile prefetch.
 #pragma unroll
         for (int ks = 0; ks < 32; ++ks) asm volatile("" : "+v"(qf[ks]));
-        const uint16_t* qp = a.q_pe + qrow * kDRope + g * 8;
+        if (lo) {  // the rotary k-steps belong to the first half
+          const uint16_t* qp = a.q_pe + qrow * kDRope + g * 8;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          *reinterpret_cast<bf16x8*>(smem + kQpeOff + wave * 4096 + ks * 1024 + lane * 16) =
-              *reinterpret_cast<const bf16x8*>(qp + ks * 16);
-      } else if (attempt == 0) {
-        // Waves 2 and 3 of a one-node workgroup only keep the workgroup's schedule: their
-        // scores are never read.  Zero queries make their score products draw far less power
-        // than a second copy of the real ones (the launch is power-bound).
-#pragma unroll
-        for (int ks = 0; ks < 32; ++ks) qf[ks] = bf16x8{};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          *reinterpret_cast<bf16x8*>(smem + kQpeOff + wave * 4096 + ks * 1024 + lane * 16) = bf16x8{};
+          for (int ks = 0; ks < 4; ++ks)
+            *reinterpret_cast<bf16x8*>(smem + kQpeOff + wave * 4096 + ks * 1024 + lane * 16) =
+                *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+        }
       }
       int t = t_begin;
       // first tile: sets the reference max on the first pass, no value product yet
