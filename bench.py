@@ -379,17 +379,25 @@ def summarize_trace(db: str, command: str, skip: int = 0, bench_log: str = None)
             if text.startswith("{") and '"metric"' in text:
                 line = json.loads(text)
         if line is not None:
+            def timed_avg(d):
+                t = d[skip:] if len(d) > skip else d
+                return sum(t) / len(t)
             verify = [d for name, d in per.items() if "verify_attn_kernel" in name]
+            merge = [d for name, d in per.items() if "verify_combine_kernel" in name]
             lines += ["", f"bench line printed by the profiled command: {json.dumps(line)}"]
             if verify and "detail" in line and "flop_visible_pairs" in line["detail"]:
-                d = verify[0]
-                timed = d[skip:] if len(d) > skip else d
-                avg = sum(timed) / len(timed)
-                frac = line["detail"]["flop_visible_pairs"] / (avg * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
+                flop = line["detail"]["flop_visible_pairs"]
+                avg = timed_avg(verify[0])
+                # one verify call = the attention kernel plus, when a group is split, one merge
+                call = avg + (timed_avg(merge[0]) if merge and len(merge[0]) == len(verify[0]) else 0.0)
+                frac = flop / (avg * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
+                frac_call = flop / (call * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
                 lines += [f"verify_attn_kernel avg_timed_us (trace): {avg:.2f}",
-                          f"verify_us_per_call (line, HIP events): {line['detail'].get('verify_us_per_call')}",
-                          f"roofline frac from the trace average: {frac:.4f}; from the line: "
-                          f"{line.get('roofline', {}).get('frac')}"]
+                          f"verify call (attention kernel + merge kernel) avg_timed_us (trace): {call:.2f}",
+                          f"verify_us_per_call (line, HIP events around each call): "
+                          f"{line['detail'].get('verify_us_per_call')}",
+                          f"roofline frac from the trace: kernel alone {frac:.4f}, whole call {frac_call:.4f}; "
+                          f"from the line (whole call): {line.get('roofline', {}).get('frac')}"]
     return "\n".join(lines) + "\n"
 
 
