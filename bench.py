@@ -130,6 +130,11 @@ def host_info() -> dict:
             h.update(f.encode())
             h.update(open(os.path.join(d, f), "rb").read())
     info["library_source_sha256"] = h.hexdigest()[:16]
+    build_info = os.path.join(ROOT, "tree_verify_mla_absorb_amd", "libddtree.build.json")
+    if os.path.exists(build_info):  # written by the build next to the library
+        b = json.load(open(build_info))
+        info["library_built_from_git_head"] = b.get("git_head")
+        info["library_built_dirty"] = b.get("git_dirty")
     try:
         info["rocm_version"] = open("/opt/rocm/.info/version").read().strip()
     except OSError:

@@ -62,7 +62,33 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout.decode(errors='replace')}")
     os.replace(tmp, LIB)
+    write_build_info()
     return LIB
+
+
+BUILD_INFO = os.path.join(PKG, "libddtree.build.json")
+
+
+def write_build_info() -> None:
+    """Record what the library was built from next to it (git HEAD when the tree is a checkout,
+    the compiler's version line), so that a copy of the tree without its history still says."""
+    import json
+
+    def run(cmd):
+        try:
+            r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True, timeout=30)
+            return r.stdout.strip() if r.returncode == 0 else None
+        except (OSError, subprocess.SubprocessError):
+            return None
+
+    info = {
+        "git_head": run(["git", "-C", ROOT, "rev-parse", "HEAD"]),
+        "git_dirty": bool(run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"])),
+        "hipcc": (run([hipcc(), "--version"]) or "").splitlines()[0:1],
+        "arch": ARCH,
+    }
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f)
 
 
 if __name__ == "__main__":
