@@ -109,9 +109,6 @@ constexpr int kDmaInScores = 7;
 constexpr int kSplitStep = 18;
 constexpr int kDmaEveryHalf = 3;
 constexpr int kDmaInHalf = 6;
-// s_waitcnt immediate for lgkmcnt(0) alone (vmcnt and expcnt at their maximum): the exchange
-// barrier waits for this wave's LDS writes, not for the staging in flight.
-constexpr int kWaitLgkmcnt0 = 0xC07F;
 // Value step that reads the probabilities of the second 16-key slice.
 constexpr int kP1Step = 3;
 
@@ -538,6 +535,8 @@ verify_attn_kernel(VerifyArgs a) {
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) xb[i4 * 64] = F32x4{st[4 * i4], st[4 * i4 + 1], st[4 * i4 + 2], st[4 * i4 + 3]};
         }
+        // lgkmcnt(0) only: this wave's LDS writes are done; vmcnt is left alone, so the next
+        // tile's staging stays in flight across the barrier
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
