@@ -130,7 +130,8 @@ int ddtree_verify_attn_ex(const void* q_lat, const void* q_pe, const void* ckv, 
  * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  The call itself allocates nothing: the split partials go
  * to a scratch array inside the library, DDTREE_NOALLOC_SCRATCH_BYTES on every GPU the library
- * runs on, held until the process ends.
+ * runs on, held until the process ends; the first call for a GPU (the GPU of `stream`) looks
+ * up that GPU's address of the array, with that GPU made current for the lookup only.
  *   num_splits  0 = the best automatic plan whose partials fit in the scratch array (the
  *               unsplit plan needs none); a forced count (n >= 1) whose partials do not fit
  *               returns DDTREE_ERR_WORKSPACE (ddtree_verify_attn_workspace_size gives the bytes).

@@ -52,6 +52,23 @@ def test_noalloc_matches_ex_on_two_calls_in_a_row(lib):
     assert_close(o2, l2, ro, rl, "noalloc, second call")
 
 
+def test_noalloc_on_a_side_stream(lib):
+    """The scratch address is looked up for the GPU of the stream the call runs on; a call on a
+    torch side stream equals ddtree_verify_attn_ex on the same stream, bitwise."""
+    print("[noalloc] S=1 P=500 Q=17 splits=4 on a side stream", flush=True)
+    b, (ql, qp, c, k, par) = inputs(64, 1, 500, 17)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o1, l1 = lib.verify_attn_ex(ql, qp, c, k, 500, par, num_splits=4, stream=side)
+        o2, l2 = lib.verify_attn_noalloc(ql, qp, c, k, 500, par, num_splits=4, stream=side)
+    side.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32)) and torch.equal(l1.view(torch.int32),
+                                                                                    l2.view(torch.int32))
+    ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, 500, b.parents)
+    assert_close(o2.cpu().numpy(), l2.cpu().numpy(), ro, rl, "noalloc, side stream")
+
+
 def test_noalloc_plan_falls_back_to_fit_the_scratch(lib):
     # the automatic plan of ddtree_verify_attn_ex needs more than the scratch holds here
     print("[noalloc] S=2 P=4096 Q=64 auto (fallback plan)", flush=True)

@@ -212,7 +212,8 @@ namespace {
 // Split partials of ddtree_verify_attn_noalloc, for callers that cannot allocate: one array per
 // GPU, held until the process ends.  Host code never passes the array's name to a kernel (on the
 // host it only stands in for the symbol); it passes the device address that hipGetSymbolAddress
-// reports for the current GPU, looked up once per device.
+// reports for the GPU the launch runs on (the stream's), looked up once per device with that
+// device current.
 constexpr size_t kScratchBytes = DDTREE_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
@@ -220,14 +221,26 @@ constexpr int kMaxDevices = 64;
 std::mutex scratch_mu;
 void* scratch_dev[kMaxDevices] = {};
 
-// The current GPU's scratch address, or an error code.
-int scratch_address(void** out) {
+// The scratch address on the GPU of `stream` (the current GPU for the null stream), or an error
+// code.  The first call for a device makes that device current for the lookup and restores the
+// caller's device afterwards.
+int scratch_address(hipStream_t stream, void** out) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DDTREE_ERR_HIP;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return DDTREE_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return DDTREE_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return DDTREE_ERR_HIP;
   std::lock_guard<std::mutex> lock(scratch_mu);
   if (scratch_dev[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return DDTREE_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return DDTREE_ERR_HIP;
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DDTREE_ERR_HIP;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return DDTREE_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return DDTREE_ERR_HIP;
     scratch_dev[dev] = p;
   }
   *out = scratch_dev[dev];
@@ -301,7 +314,7 @@ int verify_impl(const void* q_lat, const void* q_pe, const void* ckv, const void
     workspace = nullptr;
     workspace_bytes = 0;
     if (need > 0) {
-      const int rc = scratch_address(&workspace);
+      const int rc = scratch_address(stream, &workspace);
       if (rc != DDTREE_OK) return rc;
       workspace_bytes = kScratchBytes;
     }
