@@ -211,3 +211,35 @@ def test_low_side_second_pass_from_a_fully_masked_first_tile(lib):
     assert -270 < rl[0, 50].max() < -250 and rl[0, 50].min() > -270  # node 50's own row dominates
     assert rl.max() < -200
     assert_close(out, lse, ro, rl, "low-side second pass")
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_many_streams(lib, splits):
+    """A wide launch: 603 streams (not a multiple of the 8 per-XCD runs, so the runs differ in
+    length by one), prefix 40, q_len 5 (two node pairs and the odd node).  Every output is
+    finite; 40 streams spread over the batch, the first and the last included, are compared
+    with the oracle element by element."""
+    s_count, p, q = 603, 40, 5
+    b = synth.random_inputs(47, s_count, p, q)
+    idx = sorted(set(np.linspace(0, s_count - 1, 40).astype(int).tolist()))
+    _say(f"[verify] many streams S={s_count} P={p} Q={q} splits={splits}")
+    out, lse = run(lib, b, p, splits)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, p, b.parents, streams=idx)
+    assert_close(out[idx], lse[idx], ro, rl, f"many streams, splits={splits}")
+
+
+def test_zero_queries_give_the_mean_of_the_visible_rows(lib):
+    """With q_lat = q_pe = 0 every visible score is 0: out is the plain mean of the visible c_kv
+    rows and lse = ln(prefix + depth + 1), in closed form, checked against the oracle and against
+    the closed form itself, unsplit and split."""
+    b = synth.random_inputs(48, 3, 333, 17)
+    b.q_lat[:] = 0
+    b.q_pe[:] = 0
+    depth = np.stack([oracle.tree_depths(par) for par in b.parents])
+    for splits in (1, 5):
+        out, lse = run(lib, b, 333, splits)
+        ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, 333, b.parents)
+        assert_close(out, lse, ro, rl, f"zero queries, splits={splits}")
+        closed = np.log(333.0 + depth + 1.0)[:, :, None].repeat(64, axis=2)
+        assert np.abs(lse - closed).max() < 1e-5
