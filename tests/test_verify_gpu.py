@@ -243,3 +243,34 @@ def test_zero_queries_give_the_mean_of_the_visible_rows(lib):
         assert_close(out, lse, ro, rl, f"zero queries, splits={splits}")
         closed = np.log(333.0 + depth + 1.0)[:, :, None].repeat(64, axis=2)
         assert np.abs(lse - closed).max() < 1e-5
+
+
+def test_second_pass_in_one_node_workgroups(lib):
+    """Both triggers of the exact-max second pass inside the workgroups of the odd node (whose
+    two head blocks split their score chain over two waves each):
+    high side -- q_len 3, a key late in the prefix scores ~100 (natural log) above the rest for
+    one head of node 2 (the odd node);
+    low side -- q_len 63, prefix 48, two splits of two tiles: node 62, a child of the root, finds
+    split 1's first tile fully masked (reference max 0) while its visible scores sit near -259."""
+    # high side
+    b = synth.random_inputs(49, 2, 900, 3)
+    qp = oracle.bf16_bits_to_f64(b.q_pe)[1]
+    b.kpe[1, 700] = synth.f32_to_bf16_bits((24.0 * qp[2, 5]).astype(np.float32))
+    for splits in (1, 4):
+        out, lse = run(lib, b, 900, splits)
+        ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, 900, b.parents)
+        assert rl[1, 2, 5] > 100.0
+        assert_close(out, lse, ro, rl, f"one-node high side, splits={splits}")
+    # low side
+    b = synth.random_inputs(50, 1, 48, 63)
+    par = b.parents[0]
+    par[62] = 0
+    b.q_pe[:] = synth.f32_to_bf16_bits(np.full(b.q_pe.shape, 8.0, np.float32))
+    kpe = np.full(b.kpe.shape, -8.0, np.float32)
+    kpe[0, 48 + 62] = -7.0
+    b.kpe[:] = synth.f32_to_bf16_bits(kpe)
+    assert lib.num_splits(48, 63, 1, 2) == 2
+    out, lse = run(lib, b, 48, splits=2)
+    ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, 48, b.parents)
+    assert -270 < rl[0, 62].min() and rl[0, 62].max() < -250 and rl.max() < -200
+    assert_close(out, lse, ro, rl, "one-node low side")
