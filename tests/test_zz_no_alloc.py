@@ -2,8 +2,8 @@
 keeps its split partials in the library's own scratch array.  Its outputs must equal those of
 ddtree_verify_attn_ex (same plan, same kernels: bitwise) and meet the oracle's bars, on two calls
 in a row (the second smaller, so it runs over the first call's leftovers in the scratch), with a
-plan that falls back to fit the scratch, and a forced split count too large for it is refused
-before anything is launched."""
+plan that falls back to fit the scratch, and under HIP graph capture; a forced split count too
+large for the scratch is refused before anything is launched."""
 import numpy as np
 import pytest
 import torch
@@ -91,3 +91,39 @@ def test_noalloc_refuses_a_forced_plan_larger_than_the_scratch(lib):
     with pytest.raises(lib.DDTreeError) as e:
         lib.verify_attn_noalloc(ql, qp, c, k, p, par, num_splits=64)
     assert e.value.code == lib.ERR_WORKSPACE
+
+
+def test_noalloc_under_graph_capture(lib):
+    """Captured once, replayed three times with eager work on the same scratch in between (an
+    eager no-alloc call on other inputs, outputs refilled with NaN): every replay reproduces the
+    eager result bit for bit."""
+    print("[noalloc] graph capture S=2 P=700 Q=9", flush=True)
+    b, (ql, qp, c, k, par) = inputs(65, 2, 700, 9)
+    assert lib.num_splits(700, 9, 2, 0) > 1  # the partials go through the scratch
+    out = torch.empty((2, 9, 64, 512), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((2, 9, 64), dtype=torch.float32, device="cuda:0")
+    lib.verify_attn_noalloc(ql, qp, c, k, 700, par, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, 700, b.parents)
+    assert_close(ref_o.cpu().numpy(), ref_l.cpu().numpy(), ro, rl, "noalloc eager")
+    # other inputs for the eager calls between replays (they overwrite the scratch)
+    _, t2 = inputs(66, 3, 300, 17)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # a warm-up call on a side stream before capture
+        lib.verify_attn_noalloc(ql, qp, c, k, 700, par, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.verify_attn_noalloc(ql, qp, c, k, 700, par, out=out, lse=lse)
+    for replay in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        lib.verify_attn_noalloc(*t2[:4], 300, t2[4], num_splits=3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref_o.view(torch.int32)), replay
+        assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32)), replay
