@@ -10,7 +10,9 @@ Prints one JSON line.  ``value`` is TFLOP/s of the verify attention counted over
 (query, key) pairs only, divided by the whole step time (verify + accept + compaction).  The
 ``detail`` object also carries per-call times of ``ddtree_tree_accept`` over the stream and
 budget grid the pages report, of the fused call, of ``ddtree_compact_kv`` alone, and of
-``ddtree_tree_build`` (depth 15, top-8) for 1/8/64 requests and budgets 8/32/63.
+``ddtree_tree_build`` (depth 15, top-8) for 1/8/64 requests and budgets 8/32/63, and the verify
+throughput against the peak scaled to the shader clock that amdsmi reads during a few seconds of
+back-to-back calls (``detail.sustained``).
 """
 from __future__ import annotations
 
@@ -182,6 +184,69 @@ def time_calls(fn, n: int = 100, replays: int = 5) -> float:
         torch.cuda.synchronize()
         best = min(best, a.elapsed_time(b) / n * 1e3)
     return best
+
+
+PEAK_CLOCK_MHZ = 2400.0  # the shader clock the dense bf16 peak is quoted at
+
+
+def clock_summary(samples, us_per_call: float, flops: float, skip_s: float = 1.1) -> dict:
+    """Verify throughput against the dense bf16 peak scaled to the shader clock the part held.
+
+    ``samples`` are (seconds since the load started, GFX clock MHz, socket power W) read on the host
+    while the load ran.  amdsmi's readings are averages over a period of up to a second, so the
+    first ``skip_s`` seconds (which still show the idle part) are left out.  The peak scales with
+    the clock: 2500 TFLOP/s at 2400 MHz."""
+    kept = [s for s in samples if s[0] >= skip_s and s[1] > 0] or [s for s in samples if s[1] > 0]
+    if not kept:
+        return {"error": "no clock samples"}
+    clk = float(np.median([s[1] for s in kept]))
+    pw = [s[2] for s in kept if s[2] > 0]
+    achieved = flops / (us_per_call * 1e-6) / 1e12
+    peak_at = PEAK_BF16_TFLOPS * clk / PEAK_CLOCK_MHZ
+    return {"verify_us_per_call": round(us_per_call, 2), "gfx_clock_mhz_median": round(clk, 1),
+            "gfx_clock_mhz_range": [round(min(s[1] for s in kept), 1), round(max(s[1] for s in kept), 1)],
+            "socket_power_w_median": round(float(np.median(pw)), 1) if pw else None,
+            "samples": len(kept), "tflops": round(achieved, 2), "peak_at_clock_tflops": round(peak_at, 1),
+            "frac_at_clock": round(achieved / peak_at, 4)}
+
+
+def sustained_clock(fn, flops: float, seconds: float = 3.0, per_graph: int = 20) -> dict:
+    """Back-to-back calls of ``fn`` for about ``seconds`` (replays of one HIP graph of ``per_graph``
+    calls), with the GFX clock and socket power read through amdsmi while they run."""
+    import torch
+    try:
+        torch.cuda.clock_rate(0)
+        torch.cuda.power_draw(0)
+    except Exception as e:  # amdsmi missing or not permitted: no figure rather than a guess
+        return {"error": f"{type(e).__name__}: {str(e)[:100]}"}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    reps = max(1, int(seconds / (a.elapsed_time(b) * 1e-3)))
+    a.record()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    samples = []
+    while not b.query():
+        samples.append((time.perf_counter() - t0, float(torch.cuda.clock_rate(0)), float(torch.cuda.power_draw(0))))
+        time.sleep(0.05)
+    torch.cuda.synchronize()
+    return clock_summary(samples, a.elapsed_time(b) * 1e3 / (reps * per_graph), flops)
 
 
 def accept_table(lib, dev):
@@ -582,6 +647,10 @@ def main() -> int:
         compact_moved = 2 * (512 + 64) * 2 * sum(int((b.keep[s, :b.n_keep[s]] != np.arange(b.n_keep[s])).sum())
                                                  for s in range(w.streams))
         tables = {
+            "sustained": sustained_clock(
+                lambda: _lib.verify_attn_ex(q_lat, q_pe, ckv, kpe, w.prefix, parents, out=out, lse=lse,
+                                            num_splits=args.num_splits, workspace=ws),
+                2.0 * w.heads * (576 + 512) * visible_pairs(b.parents, w.prefix)),
             "accept_compact_us_per_call": round(fused_us, 2),
             "compact_kv_us_per_call": round(compact_us, 2),
             "compact_kv_moved_bytes": compact_moved,

@@ -74,3 +74,16 @@ def test_trace_summary_leaves_out_warmup(tmp_path):
     line = [l for l in text.splitlines() if l.startswith("k ")][0].split()
     calls, avg, avg_timed = int(line[1]), float(line[2]), float(line[3])
     assert calls == 3 and avg == pytest.approx(3.0) and avg_timed == pytest.approx(2.0)
+
+
+def test_clock_summary_scales_the_peak_with_the_clock():
+    # 1.2e12 FLOP in 1000 us = 1200 TFLOP/s; at a median of 1920 MHz the peak is 2500 * 0.8 = 2000
+    samples = [(0.1, 95.0, 244.0), (1.5, 1900.0, 1390.0), (1.7, 1920.0, 1395.0), (1.9, 1940.0, 1400.0),
+               (2.1, 0.0, 0.0)]
+    r = bench.clock_summary(samples, 1000.0, 1.2e12)
+    assert r["samples"] == 3 and r["gfx_clock_mhz_median"] == 1920.0 and r["gfx_clock_mhz_range"] == [1900.0, 1940.0]
+    assert r["socket_power_w_median"] == 1395.0
+    assert r["tflops"] == 1200.0 and r["peak_at_clock_tflops"] == 2000.0 and r["frac_at_clock"] == 0.6
+    assert bench.clock_summary([], 1000.0, 1.2e12) == {"error": "no clock samples"}
+    # a load shorter than the reading period still reports what it saw
+    assert bench.clock_summary([(0.1, 2100.0, 800.0)], 1000.0, 1.2e12)["samples"] == 1
