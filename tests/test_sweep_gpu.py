@@ -2,7 +2,8 @@
 
 Each case draws its stream count, prefix length(s), q_len (1..64) and split request (automatic or
 forced, so that both merge chunk widths and both workgroup groups are exercised) from a fixed
-seed, then compares every output element with the oracle at the parity bars.
+seed, then compares every output element with the oracle at the parity bars.  A third family adds
+cache strides past the tree block and explicit softmax scales.
 """
 import sys
 
@@ -59,3 +60,35 @@ def test_random_ragged_shapes(lib, i):
     torch.cuda.synchronize()
     ro, rl = oracle.verify_attn_ragged(q_lat, q_pe, ckv, kpe, prefixes, par)
     assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, f"ragged sweep {i}")
+
+
+def _padded_case(i):
+    rng = np.random.default_rng([20261205, i])
+    return (int(rng.integers(1, 13)), int(rng.integers(0, 3001)), int(rng.integers(1, 65)),
+            int(rng.choice([0, 0, 1, 2, 3, 4, 6, 8, 13, 17, 33, 64])), int(rng.choice([1, 31, 200])),
+            float(rng.choice([0.0, 0.03, 0.11])))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_padded_scaled_shapes(lib, i):
+    """Longer prefixes, a cache stride past the tree block (the rows between are bf16 NaN, which
+    no call may read) and explicit softmax scales; the no-alloc entry point, where the plan fits
+    its scratch, bitwise equal to the workspace one."""
+    s, p, q, splits, pad, scale = _padded_case(i)
+    _say(f"[padded sweep {i}] S={s} P={p} Q={q} splits={splits} pad={pad} scale={scale}")
+    b = synth.random_inputs(9000 + i, s, p, q)
+    rows = p + q
+    ckv = np.full((s, rows + pad, 512), 0x7FC0, np.uint16)
+    kpe = np.full((s, rows + pad, 64), 0x7FC0, np.uint16)
+    ckv[:, :rows], kpe[:, :rows] = b.ckv, b.kpe
+    args = (dev_bf16(b.q_lat), dev_bf16(b.q_pe), dev_bf16(ckv), dev_bf16(kpe), p, dev_i32(b.parents))
+    out, lse = lib.verify_attn_ex(*args, num_splits=splits, scale=scale)
+    if lib.workspace_size(p, q, s, splits) <= lib.NOALLOC_SCRATCH_BYTES:
+        o2, l2 = lib.verify_attn_noalloc(*args, num_splits=splits, scale=scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.view(torch.int32), out.view(torch.int32))
+        assert torch.equal(l2.view(torch.int32), lse.view(torch.int32))
+    torch.cuda.synchronize()
+    ro, rl = oracle.verify_attn(b.q_lat, b.q_pe, b.ckv, b.kpe, p, b.parents,
+                                **({"scale": scale} if scale else {}))
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, f"padded sweep {i}")

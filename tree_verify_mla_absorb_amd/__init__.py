@@ -6,6 +6,7 @@ The compute lives in ``libddtree.so`` (C ABI, ``include/ddtree.h``); this packag
     from tree_verify_mla_absorb_amd import verify_attn, verify_attn_ex, tree_accept, accept_compact, compact_kv
 """
 from ._lib import (  # noqa: F401
+    NOALLOC_SCRATCH_BYTES,
     DDTreeError,
     accept_compact,
     accept_compact_layers,
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     tree_build,
     verify_attn,
     verify_attn_ex,
+    verify_attn_noalloc,
     verify_attn_ragged,
     version,
     workspace_size,
