@@ -160,7 +160,7 @@ def host_info() -> dict:
 
 def time_calls(fn, n: int = 100, replays: int = 5) -> float:
     """Microseconds per call of ``fn`` on the GPU: ``n`` calls captured in one HIP graph (so the
-    host's per-call overhead drops out), replayed ``replays`` times, best replay."""
+    host's per-call overhead drops out), replayed ``replays`` times, median replay."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -175,15 +175,15 @@ def time_calls(fn, n: int = 100, replays: int = 5) -> float:
             fn()
     g.replay()
     torch.cuda.synchronize()
-    best = float("inf")
+    times = []
     for _ in range(replays):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         g.replay()
         b.record()
         torch.cuda.synchronize()
-        best = min(best, a.elapsed_time(b) / n * 1e3)
-    return best
+        times.append(a.elapsed_time(b) / n * 1e3)
+    return float(np.median(times))
 
 
 PEAK_CLOCK_MHZ = 2400.0  # the shader clock the dense bf16 peak is quoted at
@@ -328,7 +328,7 @@ MALL_BYTES = 256 << 20  # the part's last-level cache (Infinity Cache)
 
 def workloads_table(lib, dev, skip: str, with_oracle: bool = True):
     """``ddtree_verify_attn_ex`` (automatic split plan) us/call, TFLOP/s and % of the bf16 peak on
-    every named workload but ``skip``: 100 calls in one HIP graph, best of 5 replays.  These
+    every named workload but ``skip``: 100 calls in one HIP graph, median of 5 replays.  These
     workloads fit in the last-level cache, so that figure is warm; ``cold_us_per_call`` rotates
     through copies of the inputs and outputs totalling at least twice that cache, one copy per
     call, so that every call finds its data evicted.  With ``with_oracle``, each entry also gives
