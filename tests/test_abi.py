@@ -280,7 +280,7 @@ def test_automatic_split_plan_on_the_five_workloads():
     sweep of forced split counts on the GPU; the reported count is the larger group's."""
     assert _lib.num_splits(256, 9, 1, 0) == 5        # one stream, 9 tiles: 5 splits of 2, one merge
     assert _lib.num_splits(1024, 33, 8, 0) == 1      # 136 workgroups fit at once: no split
-    assert _lib.num_splits(1024, 9, 64, 0) == 4      # the odd node split 4 ways, pairs whole
+    assert _lib.num_splits(1024, 9, 64, 0) == 3      # the odd node split 3 ways (11 tiles each), pairs whole
     assert _lib.num_splits(4096, 33, 1, 0) == 10     # one long stream: 10 splits of 13 tiles
     assert _lib.num_splits(4096, 33, 64, 0) == 4     # 1024 pair workgroups = 4 rounds; odd node x4
     assert _lib.workspace_size(1024, 33, 8, 0) == 0  # unsplit: no workspace
@@ -293,6 +293,7 @@ def test_automatic_split_plan_on_the_five_workloads():
     assert _lib.workspace_size(4096, 33, 1, 0) == ws(2048, 10, 64, 10)
     assert _lib.workspace_size(256, 9, 1, 0) == ws(512, 5, 64, 5)
     assert _lib.workspace_size(4096, 33, 64, 0) == ws(0, 1, 64 * 64, 4)
+    assert _lib.workspace_size(1024, 9, 64, 0) == ws(0, 1, 64 * 64, 3)
 
 
 def noalloc(q_lat=A, q_pe=B, ckv=C, kpe=D, prefix=100, parents=E, q=9, s=2, out=F, lse=G, splits=0, status=None):

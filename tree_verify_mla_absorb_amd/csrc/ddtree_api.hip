@@ -123,31 +123,52 @@ Plan make_plan(int prefix_len, int q_len, int n_streams, int num_splits, size_t 
     set_splits(p, 1, num_splits);
   } else {
     const int cus = cu_count();
+    // Group 1's candidate split counts, normalised once: 1..8 and the larger powers of two
+    // (plus, per group-0 count below, that count: the odd node's workgroups then run as long as
+    // the pairs').
+    int c_splits[12], c_tps[12], n_cand = 0;
+    auto add_candidate = [&](int want) {
+      Plan q = p;
+      set_splits(q, 1, want);
+      for (int k = 0; k < n_cand; ++k)
+        if (c_splits[k] == q.splits[1] && c_tps[k] == q.tiles_per_split[1]) return;
+      c_splits[n_cand] = q.splits[1];
+      c_tps[n_cand] = q.tiles_per_split[1];
+      ++n_cand;
+    };
+    if (units1 == 0) {
+      add_candidate(1);
+    } else {
+      for (int s1 = 1; s1 <= 8; ++s1) add_candidate(s1);
+      for (int s1 = 16; s1 <= kMaxSplits; s1 *= 2) add_candidate(s1);
+    }
     double best = 1e300;
     Plan trial = p;
+    auto consider = [&](int splits1, int tps1) {
+      trial.splits[1] = splits1;
+      trial.tiles_per_split[1] = tps1;
+      if (ws_cap != (size_t)-1) {
+        finish_plan(trial, units0, units1);
+        if (workspace_bytes_for(trial) > ws_cap) return;
+      }
+      const double c = plan_cost(trial, units0, units1, cus);
+      if (c < best - 1e-9) {
+        best = c;
+        p.splits[0] = trial.splits[0];
+        p.tiles_per_split[0] = trial.tiles_per_split[0];
+        p.splits[1] = trial.splits[1];
+        p.tiles_per_split[1] = trial.tiles_per_split[1];
+      }
+    };
     for (int s0 = 1; s0 <= 32 && s0 <= p.n_tiles; ++s0) {
       if (units0 == 0 && s0 > 1) break;
       set_splits(trial, 0, s0);
       if (trial.splits[0] != s0) continue;
-      // group 1: powers of two, and group 0's own count (the odd node's workgroups then run as
-      // long as the pairs')
-      int cand[8], n_cand = 0;
-      for (int s1 = 1; s1 <= kMaxSplits && s1 <= p.n_tiles; s1 *= 2) cand[n_cand++] = s1;
-      if ((s0 & (s0 - 1)) != 0) cand[n_cand++] = s0;
-      for (int ci = 0; ci < n_cand; ++ci) {
-        const int s1 = cand[ci];
-        if (units1 == 0 && s1 > 1) break;
-        set_splits(trial, 1, s1);
-        finish_plan(trial, units0, units1);
-        if (workspace_bytes_for(trial) > ws_cap) continue;
-        const double c = plan_cost(trial, units0, units1, cus);
-        if (c < best - 1e-9) {
-          best = c;
-          p.splits[0] = trial.splits[0];
-          p.tiles_per_split[0] = trial.tiles_per_split[0];
-          p.splits[1] = trial.splits[1];
-          p.tiles_per_split[1] = trial.tiles_per_split[1];
-        }
+      for (int k = 0; k < n_cand; ++k) consider(c_splits[k], c_tps[k]);
+      if (units1 != 0 && s0 > 8 && (s0 & (s0 - 1)) != 0) {
+        Plan q = p;
+        set_splits(q, 1, s0);
+        consider(q.splits[1], q.tiles_per_split[1]);
       }
     }
   }
